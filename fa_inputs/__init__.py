@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for exact attention, shared by the oracle side and the GPU side.
+
+This module holds no attention arithmetic: it only draws random samples and
+converts them between float32 and bfloat16 bit patterns.  Both the oracle and
+the HIP path read the same arrays from here, so the two sides see the exact same
+numbers while sharing no code that computes attention.
+
+Recipe (one reading of the pages, which print no input distribution):
+* ``numpy.random.default_rng(seed)`` (PCG64), ``standard_normal(shape,
+  dtype=float32)`` with shape ``[B, H, N, d]`` in C order, drawn in the order
+  Q, K, V, dO.
+* an optional multiplier on the samples (the 4096-token d=128 workload uses
+  0.5; a power of two, so it commutes exactly with bf16 rounding);
+* bf16 tensors are the round-to-nearest-even bf16 of those float32 samples.
+
+The shapes follow the FlashAttention-2 kernel benchmark described on the page
+"FlashAttention-2を読む：長い文脈のアテンションをGPUで効率化する仕組み", section
+「約2倍という数値の対象を確認する」 (sequence 512 to 16k, head dim 64 and 128,
+causal and non-causal, batch x sequence fixed at 16k tokens).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "draw_f32",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "make_inputs",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as ``uint16``.  NaN stays a quiet NaN.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), r)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw_f32(seed: int, shape, count: int, mult: float = 1.0) -> list[np.ndarray]:
+    """Draw ``count`` float32 arrays of ``shape`` from N(0,1) with PCG64(seed),
+    each multiplied by ``mult``, in draw order."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        a = rng.standard_normal(tuple(shape), dtype=np.float32)
+        if mult != 1.0:
+            a = (a * np.float32(mult)).astype(np.float32)
+        out.append(a)
+    return out
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, dtype, mask, input distribution."""
+
+    name: str
+    dtype: str  # "bf16" or "f32"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    mult: float = 1.0
+    seed: int = 0
+    backward: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def fwd_flops(self) -> float:
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        f = 10.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
+# The five problem sizes: one fp32 case small enough for a pure-Python check,
+# and four bf16 cases with 16k tokens and hidden size 2048.
+WORKLOADS = {
+    "f32_b1h2n128d64": Workload("f32_b1h2n128d64", "f32", 1, 2, 128, 64, False),
+    "bf16_b16h32n1024d64": Workload("bf16_b16h32n1024d64", "bf16", 16, 32, 1024, 64, False),
+    "bf16_b16h32n1024d64_causal": Workload("bf16_b16h32n1024d64_causal", "bf16", 16, 32, 1024, 64, True),
+    "bf16_b4h16n4096d128_causal_x0.5": Workload(
+        "bf16_b4h16n4096d128_causal_x0.5", "bf16", 4, 16, 4096, 128, True, mult=0.5),
+    "bf16_b1h16n16384d128_causal": Workload("bf16_b1h16n16384d128_causal", "bf16", 1, 16, 16384, 128, True),
+    "bf16_b1h16n16384d128": Workload("bf16_b1h16n16384d128", "bf16", 1, 16, 16384, 128, False),
+    "bf16_b8h16n2048d128_causal_fwdbwd": Workload(
+        "bf16_b8h16n2048d128_causal_fwdbwd", "bf16", 8, 16, 2048, 128, True, backward=True),
+}
+
+
+def make_inputs(w: Workload, with_grad: bool | None = None):
+    """Inputs of a workload as numpy arrays.
+
+    Returns a dict with ``q, k, v`` (and ``do`` when a backward is wanted):
+    for bf16 workloads each entry is a ``uint16`` array of bf16 bits, for f32
+    workloads a float32 array.  ``exact_f64(arr)`` gives the exact values.
+    """
+    if with_grad is None:
+        with_grad = w.backward
+    names = ["q", "k", "v"] + (["do"] if with_grad else [])
+    arrs = draw_f32(w.seed, w.shape, len(names), w.mult)
+    out = {}
+    for n, a in zip(names, arrs):
+        out[n] = f32_to_bf16_bits(a) if w.dtype == "bf16" else a
+    return out
+
+
+def exact_f64(a: np.ndarray) -> np.ndarray:
+    """The exact value of an input array (bf16 bits or float32) as float64."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+__all__.append("exact_f64")

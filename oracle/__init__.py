@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the GPU library.
+"""
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_forward,
+    attention_forward_rows,
+    scores,
+    softmax_rows,
+)

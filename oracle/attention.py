@@ -1,0 +1,157 @@
+"""Oracle for exact scaled dot-product attention: plain, slow, fp64, on the CPU.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it, and it shares no code with the GPU kernels.
+
+What it computes, and where that is defined:
+
+* The result is the scaled dot-product attention formula
+  Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V, printed on the page
+  "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の実践的エンジニアリング",
+  section 「標準的なAttention機構のメモリ挙動」.  The same section lays out the
+  plain three-pass way to evaluate it: form the score matrix S = Q K^T, turn it
+  into the probability matrix P = softmax(S), then form O = P V.  The oracle
+  follows those three passes, materialising S and P in full for each
+  (batch, head), which is exactly what the fast kernels avoid.
+* The softmax scale is an argument (``softmax_scale`` in the call shown in
+  section 「カスタムモデルへの組み込み：コード書き換えのポイント」 of the same
+  page); the workloads pass 1/sqrt(d).
+* ``causal`` masks key j from query i when j > i (top-left aligned square mask,
+  so the first query sees only the first key).  The pages name causal
+  attention (``causal=True`` in the call above; the causal and non-causal
+  benchmark runs in section 「約2倍という数値の対象を確認する」 of
+  "FlashAttention-2を読む：長い文脈のアテンションをGPUで効率化する仕組み") but
+  do not spell out its alignment; top-left is the reading taken.
+* LSE (the log-sum-exp of each row of masked, scaled scores, natural log) is an
+  output the pages do not mention.  It is the one number per row that lets a
+  backward pass rebuild P without storing it, which the same page describes in
+  section 「タイリング（Tiling）と再計算（Recomputation）の仕組み」.
+* The backward pass is the exact vector-Jacobian product of O with respect to
+  Q, K and V.  The pages print no formula for it; the closed form used here
+  follows from the three passes above by the chain rule (softmax Jacobian
+  diag(p) - p p^T).
+
+All arithmetic is float64.  Inputs are first widened exactly to float64.
+Matrix products use numpy's ``matmul`` (BLAS); no blocking, fusion or
+reordering is applied beyond those products.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "scores",
+    "softmax_rows",
+    "attention_forward",
+    "attention_forward_rows",
+    "attention_backward",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def scores(q: np.ndarray, k: np.ndarray, causal: bool, scale: float,
+           rows: np.ndarray | None = None) -> np.ndarray:
+    """First pass: S = scale * Q K^T for one (batch, head), masked.
+
+    ``q`` is [Nq, d] (or the selected ``rows`` of a [N, d] query matrix),
+    ``k`` is [Nk, d].  Masked entries are -inf.  ``rows`` gives the query
+    positions of the rows of ``q`` (defaults to 0..Nq-1); the causal mask
+    hides key j from the query at position i when j > i.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    s = float(scale) * (q @ k.T)
+    if causal:
+        nq, nk = s.shape
+        pos = np.arange(nq) if rows is None else np.asarray(rows)
+        hidden = np.arange(nk)[None, :] > pos[:, None]
+        s = np.where(hidden, -np.inf, s)
+    return s
+
+
+def softmax_rows(s: np.ndarray):
+    """Second pass: P = softmax(S) along each row, plus the row log-sum-exp.
+
+    The row maximum is subtracted before exponentiating; in exact arithmetic
+    that changes nothing and it keeps exp() from overflowing.  Returns
+    (P, LSE) with LSE_i = m_i + log(sum_j exp(S_ij - m_i)).
+    """
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = np.sum(e, axis=-1, keepdims=True)
+    p = e / z
+    lse = (m + np.log(z))[..., 0]
+    return p, lse
+
+
+def attention_forward(q, k, v, causal: bool, scale: float, return_p: bool = False):
+    """Exact attention over [B, H, N, d] tensors.
+
+    Returns (O [B,H,N,d], LSE [B,H,N]) in float64, and P [B,H,N,N] when
+    ``return_p`` is set (tiny inputs only).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    o = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    ps = np.empty((B, H, N, k.shape[2]), dtype=np.float64) if return_p else None
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], causal, scale)
+            p, l = softmax_rows(s)
+            o[b, h] = p @ v[b, h]  # third pass: O = P V
+            lse[b, h] = l
+            if return_p:
+                ps[b, h] = p
+    if return_p:
+        return o, lse, ps
+    return o, lse
+
+
+def attention_forward_rows(q_bh, k_bh, v_bh, rows, causal: bool, scale: float):
+    """The forward restricted to some query rows of one (batch, head).
+
+    Row i of O depends only on row i of S, so this is the same definition
+    evaluated for the listed rows only.  ``q_bh`` is [N, d]; returns
+    (O [len(rows), d], LSE [len(rows)]).
+    """
+    rows = np.asarray(rows)
+    s = scores(_f64(q_bh)[rows], k_bh, causal, scale, rows=rows)
+    p, l = softmax_rows(s)
+    return p @ _f64(v_bh), l
+
+
+def attention_backward(q, k, v, do, causal: bool, scale: float):
+    """Vector-Jacobian product of O = softmax(scale * Q K^T, masked) V.
+
+    Given dO (the gradient of a scalar loss with respect to O), returns
+    (dQ, dK, dV), all [B,H,N,d] float64.  Per (batch, head), with P from the
+    forward passes:
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))      (softmax Jacobian, row by row)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+    Masked entries have P = 0, so they contribute nothing.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    B, H = q.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], causal, scale)
+            p, _ = softmax_rows(s)
+            g = do[b, h]
+            dv[b, h] = p.T @ g
+            dp = g @ v[b, h].T
+            rowdot = np.sum(p * dp, axis=-1, keepdims=True)
+            ds = p * (dp - rowdot)
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv

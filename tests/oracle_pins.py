@@ -1,0 +1,245 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each check takes the forward (and backward) function under test, so the same
+battery runs on the real oracle (every check must pass) and on copies of it
+with a planted mistake (at least one check must fail).  The facts used:
+
+* exact closed forms derived by hand from the definition (tests/golden);
+* a pure-Python brute force with an explicit exp-and-normalise softmax;
+* invariants fixed by the mathematics: rows of P sum to one; constant V
+  gives O = V; N = 1 gives O = V; the first causal row equals V[0]; Q = 0
+  gives the mean of the visible V rows with LSE = log(#visible); the last
+  causal row equals the last non-causal row; shifting every key by w leaves O
+  unchanged and shifts LSE by scale*q.w; permuting keys with values leaves
+  the output unchanged;
+* for the backward: central finite differences of <dO, O(Q,K,V)>, an
+  independent library's autograd (torch, float64, on the CPU), and the
+  identities sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, dQ = 0 when all keys
+  are equal, and dQ = dK = 0, dV = dO when N = 1.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
+
+
+def _eval_expr(s: str) -> float:
+    """Evaluate a closed-form entry such as '3/2', '-3/4*log(3)', 'log(8)'."""
+    s = s.strip()
+    coef = Fraction(1)
+    if "*" in s:
+        c, s = s.split("*", 1)
+        coef = Fraction(c)
+    if s.startswith("-log("):
+        coef, s = -coef, s[1:]
+    if s.startswith("log(") and s.endswith(")"):
+        return float(coef) * math.log(Fraction(s[4:-1]))
+    return float(coef * Fraction(s))
+
+
+def _mat(rows):
+    return np.array([[_eval_expr(x) for x in r] for r in rows], dtype=np.float64)
+
+
+def load_golden():
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    out = []
+    for c in data["cases"]:
+        e = {"name": c["name"], "scale": _eval_expr(c["scale"]), "causal": c["causal"]}
+        for key in ("q", "k", "v", "do", "o", "dq", "dk", "dv"):
+            if key in c:
+                e[key] = _mat(c[key])[None, None]
+        e["lse"] = np.array([_eval_expr(x) for x in c["lse"]])[None, None]
+        out.append(e)
+    return out
+
+
+def brute_force_forward(q, k, v, causal, scale):
+    """Pure-Python loops: explicit scores, exp, sum and division per row."""
+    B, H, N, d = q.shape
+    dv_ = v.shape[-1]
+    o = np.zeros((B, H, N, dv_))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                js = [j for j in range(N) if not (causal and j > i)]
+                sc = [scale * sum(float(q[b, h, i, c]) * float(k[b, h, j, c]) for c in range(d)) for j in js]
+                w = [math.exp(x) for x in sc]
+                z = sum(w)
+                lse[b, h, i] = math.log(z)
+                for c in range(dv_):
+                    o[b, h, i, c] = sum(wj * float(v[b, h, j, c]) for wj, j in zip(w, js)) / z
+    return o, lse
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def forward_pin_failures(fwd, tol=1e-10) -> list[str]:
+    """Run every forward pin against ``fwd(q,k,v,causal,scale) -> (O, LSE)``.
+
+    Returns the names of the pins that fail (empty when all hold).
+    """
+    fails = []
+
+    def close(a, b, t=tol):
+        return np.all(np.isfinite(a)) and np.allclose(a, b, rtol=0, atol=t)
+
+    # hand-derived closed forms
+    for g in load_golden():
+        o, lse = fwd(g["q"], g["k"], g["v"], g["causal"], g["scale"])
+        if not (close(o, g["o"], 1e-12) and close(lse, g["lse"], 1e-12)):
+            fails.append("golden:" + g["name"])
+
+    r = _rng(11)
+    for causal in (False, True):
+        for (N, d) in ((1, 3), (4, 2), (6, 4)):
+            q, k, v = (r.standard_normal((2, 1, N, d)) for _ in range(3))
+            scale = 0.7
+            o, lse = fwd(q, k, v, causal, scale)
+            ob, lb = brute_force_forward(q, k, v, causal, scale)
+            if not (close(o, ob, 1e-12) and close(lse, lb, 1e-12)):
+                fails.append(f"brute_force:N{N}d{d}c{int(causal)}")
+
+    N, d = 9, 5
+    q, k, v = (r.standard_normal((1, 2, N, d)) for _ in range(3))
+    for causal in (False, True):
+        # constant V: every output row is that row
+        vc = np.broadcast_to(r.standard_normal((1, 2, 1, d)), (1, 2, N, d)).copy()
+        o, _ = fwd(q, k, vc, causal, 0.5)
+        if not close(o, vc):
+            fails.append(f"constant_v:c{int(causal)}")
+        # Q = 0: uniform weights over the visible keys
+        o, lse = fwd(np.zeros_like(q), k, v, causal, 0.5)
+        if causal:
+            cnt = np.arange(1, N + 1, dtype=np.float64)
+            mean = np.cumsum(v, axis=2) / cnt[None, None, :, None]
+        else:
+            cnt = np.full(N, float(N))
+            mean = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+        if not (close(o, mean) and close(lse, np.broadcast_to(np.log(cnt), lse.shape))):
+            fails.append(f"zero_query:c{int(causal)}")
+        # shifting every key by w: O unchanged, LSE shifted by scale * q.w
+        w = r.standard_normal(d)
+        o1, l1 = fwd(q, k, v, causal, 0.5)
+        o2, l2 = fwd(q, k + w, v, causal, 0.5)
+        if not (close(o1, o2, 1e-9) and close(l2 - l1, 0.5 * (q @ w), 1e-9)):
+            fails.append(f"key_shift:c{int(causal)}")
+    # N = 1: O = V and LSE = scale * q.k
+    q1, k1, v1 = (r.standard_normal((1, 1, 1, 4)) for _ in range(3))
+    for causal in (False, True):
+        o, lse = fwd(q1, k1, v1, causal, 0.3)
+        if not (close(o, v1) and close(lse, 0.3 * np.sum(q1 * k1, axis=-1))):
+            fails.append(f"n1:c{int(causal)}")
+    # first causal row: O_0 = V_0, LSE_0 = scale * q_0.k_0
+    o, lse = fwd(q, k, v, True, 0.5)
+    if not (close(o[:, :, 0], v[:, :, 0]) and close(lse[:, :, 0], 0.5 * np.sum(q[:, :, 0] * k[:, :, 0], -1))):
+        fails.append("causal_first_row")
+    # last causal row equals last non-causal row
+    oc, lc = fwd(q, k, v, True, 0.5)
+    on, ln_ = fwd(q, k, v, False, 0.5)
+    if not (close(oc[:, :, -1], on[:, :, -1]) and close(lc[:, :, -1], ln_[:, :, -1])):
+        fails.append("causal_last_row")
+    # causal output rows differ from non-causal ones before the last row
+    if close(oc[:, :, :-1], on[:, :, :-1], 1e-6):
+        fails.append("causal_has_effect")
+    # non-causal: permuting keys together with values changes nothing;
+    # permuting queries permutes the output rows
+    perm = r.permutation(N)
+    o2, l2 = fwd(q, k[:, :, perm], v[:, :, perm], False, 0.5)
+    if not (close(on, o2) and close(ln_, l2)):
+        fails.append("key_permutation")
+    o3, l3 = fwd(q[:, :, perm], k, v, False, 0.5)
+    if not (close(on[:, :, perm], o3) and close(ln_[:, :, perm], l3)):
+        fails.append("query_permutation")
+    return fails
+
+
+def _torch_vjp(q, k, v, do, causal, scale):
+    """Gradients of <dO, O> from torch autograd in float64 on the CPU."""
+    import torch
+
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * torch.matmul(tq, tk.transpose(-1, -2))
+    if causal:
+        n = s.shape[-1]
+        mask = torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1)
+        s = s.masked_fill(mask, float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), tv)
+    (o * torch.tensor(do)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _finite_diff(fwd, q, k, v, do, causal, scale, h=1e-5):
+    """Central differences of L = <dO, O(Q,K,V)> for every input element."""
+    grads = []
+    args = [q.copy(), k.copy(), v.copy()]
+    for a in range(3):
+        g = np.zeros_like(args[a])
+        it = np.nditer(args[a], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = args[a][idx]
+            args[a][idx] = old + h
+            lp = np.sum(do * fwd(*args, causal, scale)[0])
+            args[a][idx] = old - h
+            lm = np.sum(do * fwd(*args, causal, scale)[0])
+            args[a][idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def backward_pin_failures(bwd, fwd, tol=1e-10) -> list[str]:
+    """Run every backward pin against ``bwd(q,k,v,do,causal,scale) -> (dQ,dK,dV)``.
+
+    ``fwd`` is used only for the finite differences.
+    """
+    fails = []
+
+    def close(a, b, t=tol):
+        return np.all(np.isfinite(a)) and np.allclose(a, b, rtol=0, atol=t)
+
+    for g in load_golden():
+        if "dq" in g:
+            dq, dk, dv = bwd(g["q"], g["k"], g["v"], g["do"], g["causal"], g["scale"])
+            if not (close(dq, g["dq"], 1e-12) and close(dk, g["dk"], 1e-12) and close(dv, g["dv"], 1e-12)):
+                fails.append("golden:" + g["name"])
+
+    r = _rng(23)
+    for causal in (False, True):
+        N, d = 5, 3
+        q, k, v, do = (r.standard_normal((1, 2, N, d)) for _ in range(4))
+        got = bwd(q, k, v, do, causal, 0.6)
+        fd = _finite_diff(fwd, q, k, v, do, causal, 0.6)
+        if not all(close(a, b, 1e-7) for a, b in zip(got, fd)):
+            fails.append(f"finite_diff:c{int(causal)}")
+        tq = _torch_vjp(q, k, v, do, causal, 0.6)
+        if not all(close(a, b, 1e-12) for a, b in zip(got, tq)):
+            fails.append(f"torch_autograd:c{int(causal)}")
+
+        N, d = 12, 6
+        q, k, v, do = (r.standard_normal((1, 2, N, d)) for _ in range(4))
+        dq, dk, dv = bwd(q, k, v, do, causal, 0.4)
+        if not close(dk.sum(axis=2), 0.0, 1e-12):
+            fails.append(f"sum_dk_zero:c{int(causal)}")
+        if not close(dv.sum(axis=2), do.sum(axis=2), 1e-12):
+            fails.append(f"sum_dv_eq_sum_do:c{int(causal)}")
+        keq = np.broadcast_to(r.standard_normal((1, 2, 1, d)), k.shape).copy()
+        dq0, _, _ = bwd(q, keq, v, do, causal, 0.4)
+        if not close(dq0, 0.0, 1e-12):
+            fails.append(f"equal_keys_dq_zero:c{int(causal)}")
+        q1, k1, v1, do1 = (r.standard_normal((1, 1, 1, 4)) for _ in range(4))
+        dq1, dk1, dv1 = bwd(q1, k1, v1, do1, causal, 0.4)
+        if not (close(dq1, 0.0) and close(dk1, 0.0) and close(dv1, do1)):
+            fails.append(f"n1:c{int(causal)}")
+    return fails

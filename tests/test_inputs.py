@@ -1,0 +1,49 @@
+"""The seeded input generators (CPU only)."""
+import numpy as np
+import torch
+
+import fa_inputs as fi
+
+
+def test_bf16_rounding_matches_torch():
+    r = np.random.default_rng(3)
+    x = np.concatenate([
+        r.standard_normal(100000).astype(np.float32),
+        (r.standard_normal(1000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1e-40, np.inf, -np.inf], dtype=np.float32),
+        # exact ties: the low 16 bits are 0x8000
+        (np.array([0x3F808000, 0x3F818000, 0xBF808000], dtype=np.uint32)).view(np.float32),
+    ])
+    ours = fi.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = fi.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_generator_is_seeded_and_ordered():
+    w = fi.WORKLOADS["f32_b1h2n128d64"]
+    a = fi.make_inputs(w, with_grad=True)
+    b = fi.make_inputs(w, with_grad=True)
+    for n in ("q", "k", "v", "do"):
+        assert np.array_equal(a[n], b[n])
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal(w.shape, dtype=np.float32)
+    k = rng.standard_normal(w.shape, dtype=np.float32)
+    assert np.array_equal(a["q"], q) and np.array_equal(a["k"], k)
+
+
+def test_half_multiplier_commutes_with_rounding():
+    w = fi.WORKLOADS["bf16_b4h16n4096d128_causal_x0.5"]
+    small = fi.Workload("t", "bf16", 1, 1, 64, 128, True, mult=0.5)
+    full = fi.Workload("t", "bf16", 1, 1, 64, 128, True, mult=1.0)
+    a = fi.exact_f64(fi.make_inputs(small)["q"])
+    b = fi.exact_f64(fi.make_inputs(full)["q"])
+    assert np.array_equal(a, 0.5 * b)
+    assert w.mult == 0.5
+
+
+def test_workload_flop_counts():
+    w = fi.WORKLOADS["bf16_b4h16n4096d128_causal_x0.5"]
+    assert w.fwd_flops() == 4 * 4 * 16 * 4096 * 4096 * 128 / 2
+    assert w.bwd_flops() == 2.5 * w.fwd_flops()

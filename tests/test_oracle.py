@@ -1,0 +1,115 @@
+"""The fp64 oracle against facts other than itself (CPU only).
+
+Every pin lives in tests/oracle_pins.py.  Here the battery runs on the real
+oracle (all pins must hold) and on copies of the oracle with one planted
+mistake each (some pin must fail), which shows the pins would catch that kind
+of error.
+"""
+import inspect
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+from tests import oracle_pins as pins
+
+
+def test_golden_file_parses():
+    cases = pins.load_golden()
+    assert len(cases) >= 5
+    assert any("dq" in c for c in cases)
+
+
+def test_forward_pins_hold():
+    assert pins.forward_pin_failures(oracle.attention_forward) == []
+
+
+def test_backward_pins_hold():
+    assert pins.backward_pin_failures(oracle.attention_backward, oracle.attention_forward) == []
+
+
+def test_rows_of_p_sum_to_one_and_mask_is_zero():
+    r = np.random.default_rng(5)
+    q, k, v = (r.standard_normal((2, 3, 17, 8)) for _ in range(3))
+    for causal in (False, True):
+        _, _, p = oracle.attention_forward(q, k, v, causal, 0.35, return_p=True)
+        assert np.allclose(p.sum(-1), 1.0, atol=1e-13, rtol=0)
+        assert np.all(p >= 0)
+        if causal:
+            upper = np.triu(np.ones((17, 17), dtype=bool), 1)
+            assert np.all(p[..., upper] == 0.0)
+
+
+def test_forward_rows_equals_full():
+    r = np.random.default_rng(6)
+    q, k, v = (r.standard_normal((1, 1, 40, 8)) for _ in range(3))
+    rows = np.array([0, 3, 17, 39])
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, causal, 0.3)
+        orow, lrow = oracle.attention_forward_rows(q[0, 0], k[0, 0], v[0, 0], rows, causal, 0.3)
+        assert np.array_equal(o[0, 0, rows], orow)
+        assert np.array_equal(lse[0, 0, rows], lrow)
+
+
+def test_large_scores_do_not_overflow():
+    # scores near 1e3 would overflow exp() without the max subtraction
+    q = np.full((1, 1, 4, 2), 30.0)
+    k = np.full((1, 1, 4, 2), 30.0)
+    k[0, 0, 2] = 29.0
+    v = np.arange(8, dtype=np.float64).reshape(1, 1, 4, 2)
+    o, lse = oracle.attention_forward(q, k, v, False, 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.allclose(lse, 1800.0 + np.log(3 + np.exp(-60.0)), atol=1e-9)
+
+
+# --- planted mistakes ------------------------------------------------------
+
+def _mutant(func, old, new):
+    """Copy of ``func`` from the oracle module with one source substitution."""
+    src = textwrap.dedent(inspect.getsource(func))
+    assert old in src, (old, func.__name__)
+    src = src.replace(old, new, 1)
+    ns = dict(vars(oa))
+    exec(compile(src, "<mutant>", "exec"), ns)
+    return ns[func.__name__], ns
+
+
+FORWARD_MUTANTS = [
+    # (function, original text, planted mistake)
+    (oa.scores, "q @ k.T", "k @ q.T"),                                # transposed S
+    (oa.scores, "float(scale) * (q @ k.T)", "(q @ k.T)"),             # scale dropped
+    (oa.scores, "> pos[:, None]", ">= pos[:, None]"),                 # mask hides the diagonal
+    (oa.scores, "> pos[:, None]", "< pos[:, None]"),                  # mask on the wrong side
+    (oa.softmax_rows, "np.max(s, axis=-1", "np.max(s, axis=-2"),      # max over the wrong axis
+    (oa.softmax_rows, "np.sum(e, axis=-1", "np.sum(e, axis=-2"),      # normalise columns
+    (oa.softmax_rows, "(m + np.log(z))", "(np.log(z))"),              # LSE without the max
+    (oa.attention_forward, "p @ v[b, h]", "p.T @ v[b, h]"),           # P transposed in PV
+    (oa.attention_forward, "s = scores(q[b, h], k[b, h]", "s = scores(k[b, h], q[b, h]"),
+]
+
+
+@pytest.mark.parametrize("func,old,new", FORWARD_MUTANTS, ids=[m[2] for m in FORWARD_MUTANTS])
+def test_forward_pins_catch_planted_mistake(func, old, new, monkeypatch):
+    mutated, _ = _mutant(func, old, new)
+    monkeypatch.setattr(oa, func.__name__, mutated)
+    assert pins.forward_pin_failures(oa.attention_forward) != []
+
+
+BACKWARD_MUTANTS = [
+    ("p.T @ g", "p @ g"),                        # dV with P untransposed
+    ("g @ v[b, h].T", "g @ v[b, h].T * 0.5"),    # dP scaled wrongly
+    ("(dp - rowdot)", "(dp + rowdot)"),          # sign error in the softmax Jacobian
+    ("(dp - rowdot)", "(dp)"),                   # dropped term
+    ("scale * (ds @ k[b, h])", "(ds @ k[b, h])"),  # dQ without the scale
+    ("ds.T @ q[b, h]", "ds @ q[b, h]"),          # dK with dS untransposed
+    ("ds @ k[b, h]", "ds.T @ k[b, h]"),          # dQ with dS transposed
+    ("np.sum(p * dp, axis=-1", "np.sum(p * dp, axis=-2"),  # row sum over the wrong axis
+]
+
+
+@pytest.mark.parametrize("old,new", BACKWARD_MUTANTS, ids=[m[1] for m in BACKWARD_MUTANTS])
+def test_backward_pins_catch_planted_mistake(old, new):
+    mutated, _ = _mutant(oa.attention_backward, old, new)
+    assert pins.backward_pin_failures(mutated, oracle.attention_forward) != []
