@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+the forward (O and LSE) and the backward (delta pre-pass, dK/dV, dQ), each
+kernel launched through the C ABI on the current stream.  The default
+workload is B=8, H=16, N=2048, d=128, causal, bf16 (the forward+backward
+problem); ``--workload`` picks another from fa_inputs.WORKLOADS (forward-only
+workloads time the forward alone).
+
+FLOPs: forward 4*B*H*N^2*d, backward 10*B*H*N^2*d (the five N^2*d products
+of the recomputing backward), each halved for causal.  The value printed is
+the whole step's FLOPs over its wall time between two synchronisations.
+
+Each kernel is also bracketed by HIP events on the launch stream; the kernel
+with the largest average duration is reported with its roofline:
+achieved = its algorithmic FLOPs per launch / its average duration, against
+the MI355X dense bf16 matrix-core peak.
+
+cpu_baseline: the fp64 oracle (materialising S and P) timed on the host on
+the first whole heads of the same workload, forward+backward, for about
+``--cpu-seconds`` seconds.
+
+One JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+DEFAULT_WORKLOAD = "bf16_b8h16n2048d128_causal_fwdbwd"
+HEADLINE_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal"]
+
+
+def _products(w, n):
+    """FLOPs of n N^2*d products (2*N^2*d each) over all heads, halved if causal."""
+    f = 2.0 * n * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
+
+
+def cpu_baseline(w, budget_s: float):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import fa_inputs as fi
+    import oracle
+
+    x = fi.make_inputs(w, with_grad=True)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [fi.exact_f64(x[n][sl]) for n in ("q", "k", "v")]
+        oracle.attention_forward(*args, w.causal, w.scale)
+        if w.backward:
+            oracle.attention_backward(*args, fi.exact_f64(x["do"][sl]), w.causal, w.scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = (w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)) / (w.B * w.H)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": per_head * done / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (batch, head) pairs, forward{'+backward' if w.backward else ''}, "
+                  f"fp64 numpy, {dt:.1f} s, host nproc {os.cpu_count()}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-headline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the attention kernels on a single "
+              "MI355X and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_18_amd as fa
+    import fa_inputs as fi
+
+    fa._lib.load()  # raises if the HIP library is missing
+    w = fi.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 path")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = fi.make_inputs(w, with_grad=True)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    B, H, N, d, causal, scale = w.B, w.H, w.N, w.d, int(w.causal), w.scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_backward_workspace_size(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    P = {n: t.data_ptr() for n, t in dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws).items()}
+
+    kernels = [
+        ("fwd", lambda: fa.fa_forward(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, N, d, causal, scale, sp),
+         _products(w, 2)),
+    ]
+    if w.backward:
+        kernels += [
+            ("bwd_preprocess", lambda: fa.fa_backward_preprocess(P["o"], P["do"], B, H, N, d, P["ws"], ws_bytes, sp),
+             0.0),
+            ("bwd_dkdv", lambda: fa.fa_backward_dkdv(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dk"], P["dv"],
+                                                     B, H, N, d, causal, scale, P["ws"], ws_bytes, sp),
+             _products(w, 4)),
+            ("bwd_dq", lambda: fa.fa_backward_dq(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dq"], B, H, N, d,
+                                                 causal, scale, P["ws"], ws_bytes, sp),
+             _products(w, 1)),
+        ]
+    step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
+
+    def run_step(evs=None):
+        for i, (name, fn, _) in enumerate(kernels):
+            if evs is not None:
+                evs[i][0].record(stream)
+            st = fn()
+            if st != 0:
+                raise RuntimeError(f"{name}: {fa.fa_status_string(st)}")
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in kernels]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_kernel_ms = {}
+    for i, (name, _, _) in enumerate(kernels):
+        per_kernel_ms[name] = float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+    dom = max(kernels, key=lambda kk: per_kernel_ms[kk[0]])
+    dom_ms = per_kernel_ms[dom[0]]
+    achieved = dom[2] / (dom_ms * 1e-3) / 1e12
+
+    kernel_table = {n: {"ms": round(per_kernel_ms[n], 4),
+                        "tflops": round(f / (per_kernel_ms[n] * 1e-3) / 1e12, 1) if f else None}
+                    for n, _, f in kernels}
+
+    headline = []
+    if not args.no_headline:
+        for name in HEADLINE_FWD:
+            hw = fi.WORKLOADS[name]
+            hx = fi.make_inputs(hw, with_grad=False)
+            hq, hk, hv = (to_dev(hx[n]) for n in ("q", "k", "v"))
+            ho = torch.empty_like(hq)
+            hl = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=dev)
+
+            def fwd_once():
+                st = fa.fa_forward(hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), ho.data_ptr(), hl.data_ptr(),
+                                   hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale, sp)
+                assert st == 0
+
+            for _ in range(3):
+                fwd_once()
+            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a, b_ in hev:
+                a.record(stream)
+                fwd_once()
+                b_.record(stream)
+            torch.cuda.synchronize()
+            hms = float(np.mean([a.elapsed_time(b_) for a, b_ in hev]))
+            tf = hw.fwd_flops() / (hms * 1e-3) / 1e12
+            headline.append({"workload": name, "kernel": "fwd", "ms": round(hms, 4), "tflops": round(tf, 1),
+                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+            del hq, hk, hv, ho, hl
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd/bwd TFLOPs/s (bf16, d=64/128, causal) + % of MFMA bf16 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": bool(causal),
+                   "step": "forward+backward" if w.backward else "forward",
+                   "step_gflop": round(step_flops / 1e9, 2), "parallelism": "single GPU",
+                   "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)},
+        "kernels": kernel_table,
+        "headline_forward": headline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+"""Exact scaled dot-product attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libfa.so`` (include/fa.h).  The
+functions here only check and marshal arguments: every step of the
+computation runs in the HIP kernels.  PyTorch supplies device memory and the
+current stream.
+
+Tensors are [B, H, N, d], contiguous, on the GPU, either all bfloat16 or all
+float32 (the float32 path is a slower debug path).  ``scale`` defaults to
+1/sqrt(d), as ``softmax_scale=None`` does in the call shown on the page "Flash
+Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の実践的エンジニアリング",
+section 「カスタムモデルへの組み込み：コード書き換えのポイント」.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import FA_OK, FaLibraryMissing, load  # noqa: F401
+
+__all__ = [
+    "FaError",
+    "fa_forward",
+    "fa_backward",
+    "fa_forward_f32",
+    "fa_backward_f32",
+    "fa_backward_preprocess",
+    "fa_backward_dkdv",
+    "fa_backward_dq",
+    "fa_backward_workspace_size",
+    "fa_status_string",
+    "fa_abi_version",
+    "forward",
+    "backward",
+]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(fa_status_string(status))
+
+
+def _call(name: str, *args) -> int:
+    return getattr(load(), name)(*args)
+
+
+# --- raw C-ABI calls (same names as include/fa.h; pointers as ints) ---------
+
+def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
+    return _call("fa_forward", q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream)
+
+
+def fa_forward_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
+    return _call("fa_forward_f32", q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream)
+
+
+def fa_backward(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward", q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                 ws, ws_bytes, stream)
+
+
+def fa_backward_preprocess(o, do, B, H, N, d, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_preprocess", o, do, B, H, N, d, ws, ws_bytes, stream)
+
+
+def fa_backward_dkdv(q, k, v, lse, do, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_dkdv", q, k, v, lse, do, dk, dv, B, H, N, d, int(causal), float(scale), ws,
+                 ws_bytes, stream)
+
+
+def fa_backward_dq(q, k, v, lse, do, dq, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_dq", q, k, v, lse, do, dq, B, H, N, d, int(causal), float(scale), ws,
+                 ws_bytes, stream)
+
+
+def fa_backward_f32(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_f32", q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, int(causal),
+                 float(scale), ws, ws_bytes, stream)
+
+
+def fa_backward_workspace_size(B, H, N, d) -> int:
+    return int(_call("fa_backward_workspace_size", B, H, N, d))
+
+
+def fa_status_string(status: int) -> str:
+    return _call("fa_status_string", int(status)).decode()
+
+
+def fa_abi_version() -> int:
+    return int(_call("fa_abi_version"))
+
+
+# --- torch tensor wrappers -------------------------------------------------
+
+def _check(ts, names):
+    import torch
+
+    t0 = ts[0]
+    if t0.dim() != 4:
+        raise ValueError(f"{names[0]} must be [B, H, N, d], got shape {tuple(t0.shape)}")
+    if t0.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {t0.dtype}; use bfloat16 or float32")
+    for t, n in zip(ts, names):
+        if t.shape != t0.shape or t.dtype != t0.dtype:
+            raise ValueError(f"{n}: shape/dtype {tuple(t.shape)}/{t.dtype} does not match {names[0]}")
+        if not t.is_cuda or t.device != t0.device:
+            raise ValueError(f"{n} must be on the same GPU as {names[0]}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous [B, H, N, d]")
+    return t0.dtype == torch.float32
+
+
+def _stream(device):
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None):
+    """O, LSE = attention(q, k, v).  Returns (o [B,H,N,d], lse [B,H,N] float32)."""
+    import torch
+
+    f32 = _check([q, k, v], ["q", "k", "v"])
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = fa_forward_f32 if f32 else fa_forward
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+            causal, scale, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
+    """dQ, dK, dV for the incoming gradient ``do`` of attention(q, k, v)."""
+    import torch
+
+    f32 = _check([q, k, v, o, do], ["q", "k", "v", "o", "do"])
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    need = fa_backward_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fn = fa_backward_f32 if f32 else fa_backward
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

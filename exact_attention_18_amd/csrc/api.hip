@@ -1,0 +1,234 @@
+// C ABI entry points (declared in include/fa.h): argument checks on the
+// host, then dispatch to the launchers.  No allocation, no global state.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "launch.h"
+
+extern "C" size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+namespace {
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point.  Returns FA_OK or a status.
+int check_common(int B, int H, int N, int d, int causal, float scale, bool bf16, size_t* elems) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.0f) return FA_ERR_INVALID_ARG;
+  if (bf16) {
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  } else {
+    if (d > 128 || d % 4 != 0) return FA_ERR_UNSUPPORTED;
+  }
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL) return FA_ERR_INVALID_ARG;
+  const unsigned long long n = bh * (unsigned long long)N * (unsigned long long)d;
+  if (n / (unsigned long long)d / (unsigned long long)N != bh || n > (1ULL << 50))
+    return FA_ERR_INVALID_ARG;
+  *elems = (size_t)n;
+  return FA_OK;
+}
+
+// Null, alignment and overlap checks.  `ins` are read-only (may alias each
+// other); `outs` are written and must be disjoint from everything.
+int check_buffers(const Span* ins, const void* const* in_ptrs, int n_in, const Span* outs,
+                  const void* const* out_ptrs, int n_out) {
+  for (int i = 0; i < n_in; ++i)
+    if (in_ptrs[i] == nullptr || !aligned16(in_ptrs[i])) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_out; ++i)
+    if (out_ptrs[i] == nullptr || !aligned16(out_ptrs[i])) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j])) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+template <typename T>
+int forward_impl(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d,
+                 int causal, float scale, void* stream, bool bf16) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, bf16, &elems);
+  if (st != FA_OK) return st;
+  const size_t tb = elems * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
+  const void* inp[3] = {q, k, v};
+  const Span outs[2] = {span(o, tb), span(lse, lb)};
+  const void* outp[2] = {o, lse};
+  st = check_buffers(ins, inp, 3, outs, outp, 2);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if constexpr (sizeof(T) == 2)
+    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+  else
+    return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+}
+
+template <typename T>
+int backward_impl(const T* q, const T* k, const T* v, const T* o, const float* lse, const T* dO, T* dq,
+                  T* dk, T* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream, bool bf16) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, bf16, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_backward_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * sizeof(T), lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(lse, lb), span(dO, tb)};
+  const void* inp[6] = {q, k, v, o, lse, dO};
+  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
+  const void* outp[4] = {dq, dk, dv, workspace};
+  st = check_buffers(ins, inp, 6, outs, outp, 4);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  if constexpr (sizeof(T) == 2)
+    return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, B * H, N, d, causal != 0,
+                                          scale, delta, s));
+  else
+    return hip_status(fa::launch_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, B * H, N, d, causal != 0,
+                                         scale, delta, s));
+}
+
+// Shared checks of the bf16 backward stages.  `ws_written` says whether the
+// stage writes the workspace (an output) or only reads it (an input).
+int stage_checks(int B, int H, int N, int d, int causal, float scale, const void* const* in_ptrs,
+                 const size_t* in_bytes, int n_in, const void* const* out_ptrs, int n_out,
+                 const void* workspace, size_t workspace_bytes, bool ws_written) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_backward_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * 2;
+  Span ins[8], outs[4];
+  const void* inp[8];
+  const void* outp[4];
+  int ni = 0, no = 0;
+  for (int i = 0; i < n_in; ++i) {
+    ins[ni] = span(in_ptrs[i], in_bytes[i] ? in_bytes[i] : tb);
+    inp[ni++] = in_ptrs[i];
+  }
+  for (int i = 0; i < n_out; ++i) {
+    outs[no] = span(out_ptrs[i], tb);
+    outp[no++] = out_ptrs[i];
+  }
+  if (ws_written) {
+    outs[no] = span(workspace, need);
+    outp[no++] = workspace;
+  } else {
+    ins[ni] = span(workspace, need);
+    inp[ni++] = workspace;
+  }
+  return check_buffers(ins, inp, ni, outs, outp, no);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_backward_preprocess(const void* o, const void* dO, int B, int H, int N, int d, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const void* in[2] = {o, dO};
+  const size_t ib[2] = {0, 0};
+  int st = stage_checks(B, H, N, d, 0, 1.0f, in, ib, 2, nullptr, 0, workspace, workspace_bytes, true);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_rowdot_bf16(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
+                                           static_cast<float*>(workspace), (long long)B * H * N, d,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk,
+                     void* dv, int B, int H, int N, int d, int causal, float scale, const void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const void* in[5] = {q, k, v, lse, dO};
+  const size_t ib[5] = {0, 0, 0, (size_t)B * H * N * sizeof(float), 0};
+  const void* out[2] = {dk, dv};
+  int st = stage_checks(B, H, N, d, causal, scale, in, ib, 5, out, 2, workspace, workspace_bytes, false);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_bwd_dkdv_bf16(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), lse,
+      static_cast<const uint16_t*>(dO), static_cast<const float*>(workspace), static_cast<uint16_t*>(dk),
+      static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+}
+
+int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq,
+                   int B, int H, int N, int d, int causal, float scale, const void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const void* in[5] = {q, k, v, lse, dO};
+  const size_t ib[5] = {0, 0, 0, (size_t)B * H * N * sizeof(float), 0};
+  const void* out[1] = {dq};
+  int st = stage_checks(B, H, N, d, causal, scale, in, ib, 5, out, 1, workspace, workspace_bytes, false);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_bwd_dq_bf16(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), lse,
+      static_cast<const uint16_t*>(dO), static_cast<const float*>(workspace), static_cast<uint16_t*>(dq), B * H,
+      N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+}
+
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (pointer, size, scale, causal flag, alignment, overlap or workspace)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension not supported by this entry point";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  const size_t rows = (size_t)B * (size_t)H * (size_t)N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+               int d, int causal, float scale, void* stream) {
+  return forward_impl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d,
+                      causal, scale, stream, true);
+}
+
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                   int N, int d, int causal, float scale, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, stream, false);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse,
+                       static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d, causal,
+                       scale, workspace, workspace_bytes, stream, true);
+}
+
+int fa_backward_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                    const float* dO, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                    int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d, causal, scale, workspace,
+                       workspace_bytes, stream, false);
+}
+
+}  // extern "C"

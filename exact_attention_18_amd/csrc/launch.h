@@ -1,0 +1,45 @@
+// Internal launchers behind the C ABI.  Arguments are already validated:
+// tensors are [BH][N][d] contiguous (BH = batch*heads), pointers are 16-byte
+// aligned, sizes are positive and supported.  Each launcher enqueues its
+// kernels on `stream` and returns the HIP status of the launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                           float* lse, int BH, int N, int d, bool causal, float scale,
+                           hipStream_t stream);
+
+hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
+                           uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
+                           float scale, float* delta, hipStream_t stream);
+
+hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* lse, const uint16_t* dO, const float* delta,
+                                uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
+                                float scale, hipStream_t stream);
+
+hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const float* lse, const uint16_t* dO, const float* delta,
+                              uint16_t* dq, int BH, int N, int d, bool causal, float scale,
+                              hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                          const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                          int BH, int N, int d, bool causal, float scale, float* delta,
+                          hipStream_t stream);
+
+// delta[row] = sum_c dO[row][c] * O[row][c] over `rows` rows of width d.
+hipError_t launch_rowdot_bf16(const uint16_t* o, const uint16_t* dO, float* delta, long long rows,
+                              int d, hipStream_t stream);
+hipError_t launch_rowdot_f32(const float* o, const float* dO, float* delta, long long rows, int d,
+                             hipStream_t stream);
+
+}  // namespace fa

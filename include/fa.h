@@ -1,0 +1,144 @@
+/*
+ * fa.h - C ABI of the exact-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention,
+ *     O = softmax(scale * Q K^T) V,
+ * the formula given on the page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：
+ * IO最適化の実践的エンジニアリング", section 「標準的なAttention機構のメモリ挙動」, and its
+ * backward pass.  It never forms the N x N score or probability matrix in device
+ * memory: Q, K and V are processed in on-chip tiles with a running (online)
+ * softmax, as the same page describes in section 「タイリング（Tiling）と再計算
+ * （Recomputation）の仕組み」 and as the page "FlashAttention-2を読む：長い文脈の
+ * アテンションをGPUで効率化する仕組み" describes in section 「タイル分割でも全体の
+ * 正規化を保つ」.  Work is split over batch x heads x query blocks (same page,
+ * section 「GPUの稼働率を高める三つの工夫」).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout     All tensors are dense, contiguous [B][H][N][d] with d fastest
+ *            (element (b,h,i,c) at offset ((b*H + h)*N + i)*d + c).  LSE and the
+ *            backward workspace rows are [B][H][N] float32.
+ * Precision  The bf16 entry points take bfloat16 as raw 16-bit storage
+ *            (const void*), multiply in bf16 on the matrix cores and accumulate
+ *            in float32; outputs are rounded to bf16 to nearest-even.  The _f32
+ *            entry points take float32 everywhere (a slower debug path).
+ * Shapes     B, H, N >= 1.  bf16: d in {64, 128}.  f32: 4 <= d <= 128 and
+ *            d % 4 == 0.  Any N (a ragged last tile is masked).  N_q == N_k == N.
+ * scale      Finite and >= 0 (0 gives uniform attention).  The caller chooses
+ *            it; 1/sqrt(d) is the usual value.
+ * causal     0 or 1.  1 hides key j from query i when j > i (top-left aligned).
+ * LSE        lse[b][h][i] = log(sum_j exp(scale * q_i . k_j)) over the visible
+ *            keys j, natural log, float32.
+ * Ownership  The caller allocates and owns every buffer (device memory).  The
+ *            library allocates nothing and keeps no state between calls.
+ * Aliasing   q, k and v may alias one another.  Every output buffer (o, lse,
+ *            dq, dk, dv, workspace) must not overlap any other buffer passed to
+ *            the same call.
+ * Alignment  Every tensor pointer must be 16-byte aligned.
+ * Streams    Work is enqueued on `stream` (a hipStream_t passed as void*, NULL
+ *            for the default stream).  Calls return without synchronising;
+ *            results are valid once the stream has reached them.
+ * Errors     Every entry point returns FA_OK (0) or a negative status.  All
+ *            arguments are checked on the host before any HIP call; a failed
+ *            check launches nothing and writes nothing.  FA_ERR_HIP reports a
+ *            launch failure from the HIP runtime.  fa_status_string() names a
+ *            status.  No C++ exception crosses this interface.
+ * Threads    Stateless and re-entrant; calls on different streams may overlap.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, scale, causal flag,
+                              misaligned or overlapping buffers, workspace too small */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension not supported by this entry point */
+  FA_ERR_HIP = -3          /* the HIP runtime reported a launch error */
+};
+
+/*
+ * Forward pass, bf16 in/out, float32 accumulation.
+ *   q, k, v : [B][H][N][d] bf16, read only.
+ *   o       : [B][H][N][d] bf16, written: O = softmax(scale*QK^T (masked)) V.
+ *   lse     : [B][H][N] float32, written: the row log-sum-exp defined above,
+ *             which fa_backward needs.
+ * The N x N matrices live only in registers, tile by tile (pages cited above).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Backward pass, bf16 in/out, float32 accumulation: the vector-Jacobian
+ * product of O with respect to Q, K and V for the incoming gradient dO.
+ * The probability matrix is recomputed from q, k and lse rather than stored
+ * (page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の実践的
+ * エンジニアリング", section 「タイリング（Tiling）と再計算（Recomputation）の仕組み」).
+ *   q, k, v, o, dO : [B][H][N][d] bf16, read only (o from fa_forward).
+ *   lse            : [B][H][N] float32 from fa_forward with the same
+ *                    causal flag and scale.
+ *   dq, dk, dv     : [B][H][N][d] bf16, written.
+ *   workspace      : device scratch of at least fa_backward_workspace_size()
+ *                    bytes, 16-byte aligned; its contents on entry are ignored
+ *                    and on return are unspecified.
+ * Deterministic: the same inputs give bit-identical outputs (no atomics).
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages of fa_backward, as separate calls (bf16 only).  Calling
+ * fa_backward_preprocess, then fa_backward_dkdv and fa_backward_dq (in either
+ * order) on one stream with the same workspace gives exactly what
+ * fa_backward gives; they exist so that callers can time or schedule the
+ * stages one by one.  Arguments mean what they mean for fa_backward.
+ *   fa_backward_preprocess: workspace rows delta_i = sum_c dO_ic * O_ic.
+ *   fa_backward_dkdv: dK and dV, one workgroup per 128 keys, looping over
+ *     query tiles (reads q, k, v, lse, dO and the workspace).
+ *   fa_backward_dq: dQ, one workgroup per 128 queries, looping over key
+ *     tiles (reads q, k, v, lse, dO and the workspace).
+ * The same checks as fa_backward apply to every buffer each stage touches.
+ */
+int fa_backward_preprocess(const void* o, const void* dO, int B, int H, int N, int d,
+                           void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                     const void* dO, void* dk, void* dv, int B, int H, int N, int d,
+                     int causal, float scale, const void* workspace, size_t workspace_bytes,
+                     void* stream);
+int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse,
+                   const void* dO, void* dq, int B, int H, int N, int d, int causal, float scale,
+                   const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_backward and fa_backward_f32 need for these sizes
+ * (0 if a size is not positive).  Pure host function. */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/* float32 debug twins of fa_forward / fa_backward: same arguments, same
+ * layouts and semantics, float32 storage and arithmetic throughout. */
+int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, void* stream);
+int fa_backward_f32(const float* q, const float* k, const float* v, const float* o,
+                    const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                    int B, int H, int N, int d, int causal, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text naming a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

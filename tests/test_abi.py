@@ -1,0 +1,144 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (so these run with no GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_attention_18_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+INVALID, UNSUP = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+FA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.fa_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3):
+        s = lib.fa_status_string(code).decode()
+        assert s.startswith("FA_")
+    assert lib.fa_status_string(7).decode() == "unknown status"
+
+
+def test_workspace_size(lib):
+    assert lib.fa_backward_workspace_size(8, 16, 2048, 128) == 8 * 16 * 2048 * 4
+    assert lib.fa_backward_workspace_size(1, 1, 1, 64) == 256
+    assert lib.fa_backward_workspace_size(0, 1, 1, 64) == 0
+    assert lib.fa_backward_workspace_size(1, 1, -5, 64) == 0
+
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation on the host.  Each buffer sits in its own 4 GiB window.
+def ptr(i, off=0):
+    return (i + 1) << 32 | off
+
+
+def fwd(lib, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None, f32=False):
+    p = ptrs or [ptr(i) for i in range(5)]
+    fn = lib.fa_forward_f32 if f32 else lib.fa_forward
+    return fn(*p, B, H, N, d, causal, scale, None)
+
+
+def bwd(lib, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None, ws_bytes=None, f32=False):
+    p = ptrs or [ptr(i) for i in range(10)]
+    if ws_bytes is None:
+        ws_bytes = lib.fa_backward_workspace_size(B, H, N, d)
+    fn = lib.fa_backward_f32 if f32 else lib.fa_backward
+    return fn(*p[:9], B, H, N, d, causal, scale, p[9], ws_bytes, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1), dict(N=-3),
+                                dict(causal=2), dict(causal=-1), dict(scale=-0.5),
+                                dict(scale=math.inf), dict(scale=math.nan), dict(B=1 << 20, H=1 << 12)])
+def test_forward_rejects_bad_sizes(lib, kw, f32):
+    assert fwd(lib, f32=f32, **kw) == INVALID
+    assert bwd(lib, f32=f32, **kw) == INVALID
+
+
+@pytest.mark.parametrize("d", [16, 32, 96, 192, 256])
+def test_bf16_rejects_unsupported_head_dim(lib, d):
+    assert fwd(lib, d=d) == UNSUP
+    assert bwd(lib, d=d) == UNSUP
+
+
+@pytest.mark.parametrize("d", [2, 6, 130, 256])
+def test_f32_rejects_unsupported_head_dim(lib, d):
+    assert fwd(lib, d=d, f32=True) == UNSUP
+    assert bwd(lib, d=d, f32=True) == UNSUP
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("which", range(5))
+def test_forward_rejects_null_and_misaligned(lib, which, f32):
+    p = [ptr(i) for i in range(5)]
+    p[which] = None
+    assert fwd(lib, ptrs=p, f32=f32) == INVALID
+    p = [ptr(i) for i in range(5)]
+    p[which] = ptr(which, 8)
+    assert fwd(lib, ptrs=p, f32=f32) == INVALID
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_backward_rejects_null_and_misaligned(lib, which):
+    p = [ptr(i) for i in range(10)]
+    p[which] = None
+    assert bwd(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(10)]
+    p[which] = ptr(which, 4)
+    assert bwd(lib, ptrs=p) == INVALID
+
+
+def test_forward_rejects_overlapping_outputs(lib):
+    base = [ptr(i) for i in range(5)]
+    o_on_q = list(base)
+    o_on_q[3] = base[0] + 64  # o starts inside q
+    assert fwd(lib, ptrs=o_on_q) == INVALID
+    lse_in_o = list(base)
+    lse_in_o[4] = base[3] + 16  # lse inside o
+    assert fwd(lib, ptrs=lse_in_o) == INVALID
+
+
+def test_backward_rejects_overlaps_and_small_workspace(lib):
+    base = [ptr(i) for i in range(10)]
+    p = list(base)
+    p[9] = base[6]  # workspace on dq
+    assert bwd(lib, ptrs=p) == INVALID
+    p = list(base)
+    p[7] = base[5]  # dk on dO
+    assert bwd(lib, ptrs=p) == INVALID
+    need = lib.fa_backward_workspace_size(1, 1, 8, 64)
+    assert bwd(lib, ws_bytes=need - 1) == INVALID
+
+
+def test_python_binding_names_match_abi():
+    import exact_attention_18_amd as fa
+
+    for n in declared_functions():
+        assert callable(getattr(fa, n)), n
+    assert fa.fa_status_string(-1).startswith("FA_ERR_INVALID_ARG")

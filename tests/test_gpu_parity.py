@@ -1,0 +1,256 @@
+"""GPU parity: the HIP kernels (through the C ABI binding) against the fp64 oracle.
+
+Tolerances (max over all compared elements of |GPU - oracle|):
+  * bf16 I/O, float32 accumulation: O, dQ, dK, dV <= 2e-2;
+  * float32 debug path: O, dQ, dK, dV <= 1e-5;
+  * LSE <= 1e-3 on both paths.
+The oracle is evaluated on the exact values the GPU receives (bf16 bits widened
+to float64), so the difference measures only the kernels' own rounding.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.gpu_util import dev, host64, max_abs, random_inputs, storage_floor
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_18_amd as fa
+
+    fa._lib.load()  # raises if the HIP library is missing: no fallback
+    return fa
+
+
+def _run_fwd(fa, q, k, v, causal, scale):
+    import torch
+
+    o, lse = fa.forward(dev(q), dev(k), dev(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_fwd(fa, dtype, B, H, N, d, causal, seed=0, mult=1.0):
+    q, k, v = random_inputs(seed, (B, H, N, d), dtype, 3, mult)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(fa, q, k, v, causal, scale)
+    ro, rl = oracle.attention_forward(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), causal, scale)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    eo, el = max_abs(host64(o), ro), max_abs(host64(lse), rl)
+    assert eo <= tol, f"O error {eo:.3g} > {tol} (storage floor {storage_floor(ro):.3g})"
+    assert el <= (TOL_LSE if dtype == "bf16" else TOL_F32), f"LSE error {el:.3g}"
+    return eo, el
+
+
+def _check_bwd(fa, dtype, B, H, N, d, causal, seed=0, mult=1.0):
+    import torch
+
+    q, k, v, do = random_inputs(seed, (B, H, N, d), dtype, 4, mult)
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(tq, tk, tv, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), fi.exact_f64(do),
+                                    causal, scale)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    errs = [max_abs(host64(x), r) for x, r in zip((dq, dk, dv), ref)]
+    for name, e, r in zip(("dQ", "dK", "dV"), errs, ref):
+        assert e <= tol, f"{name} error {e:.3g} > {tol} (storage floor {storage_floor(r):.3g})"
+    return errs
+
+
+SMALL_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 300]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", SMALL_N + [1000])
+def test_bf16_forward_small(fa, N, d, causal):
+    _check_fwd(fa, "bf16", 2, 3, N, d, causal, seed=N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", SMALL_N)
+def test_bf16_backward_small(fa, N, d, causal):
+    _check_bwd(fa, "bf16", 2, 2, N, d, causal, seed=100 + N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [4, 64, 100, 128])
+@pytest.mark.parametrize("N", [1, 2, 17, 33, 64, 65, 129, 300])
+def test_f32_forward_small(fa, N, d, causal):
+    _check_fwd(fa, "f32", 2, 2, N, d, causal, seed=200 + N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [4, 64, 128])
+@pytest.mark.parametrize("N", [1, 2, 17, 65, 129, 300])
+def test_f32_backward_small(fa, N, d, causal):
+    _check_bwd(fa, "f32", 1, 2, N, d, causal, seed=300 + N)
+
+
+def test_f32_workload(fa):
+    """The float32 problem B=1, H=2, N=128, d=64, non-causal, seed 0, scale 1/8,
+    forward and backward at 1e-5."""
+    w = fi.WORKLOADS["f32_b1h2n128d64"]
+    _check_fwd(fa, "f32", w.B, w.H, w.N, w.d, w.causal, seed=0)
+    _check_bwd(fa, "f32", w.B, w.H, w.N, w.d, w.causal, seed=0)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_invariants_on_gpu_output(fa, dtype, causal):
+    """Pins that hold whatever the oracle says: constant V gives O = V; the
+    first causal row is V[0]; Q = 0 gives the mean of the visible rows with
+    LSE = log(#visible); sum_j exp(scale*q.k_j - LSE) = 1."""
+    B, H, N, d = 1, 2, 200, 64
+    q, k, v = random_inputs(7, (B, H, N, d), dtype, 3)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    scale = 0.125
+    # constant V
+    vc = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    o, _ = _run_fwd(fa, q, k, vc, causal, scale)
+    assert max_abs(host64(o), fi.exact_f64(vc)) <= tol
+    # Q = 0
+    z = np.zeros_like(q)
+    o, lse = _run_fwd(fa, z, k, v, causal, scale)
+    vv = fi.exact_f64(v)
+    if causal:
+        cnt = np.arange(1, N + 1, dtype=np.float64)
+        mean = np.cumsum(vv, axis=2) / cnt[None, None, :, None]
+    else:
+        cnt = np.full(N, float(N))
+        mean = np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+    assert max_abs(host64(o), mean) <= tol
+    assert max_abs(host64(lse), np.broadcast_to(np.log(cnt), (B, H, N))) <= TOL_LSE
+    # first causal row and LSE normalisation
+    o, lse = _run_fwd(fa, q, k, v, causal, scale)
+    qq, kk = fi.exact_f64(q), fi.exact_f64(k)
+    if causal:
+        assert max_abs(host64(o)[:, :, 0], vv[:, :, 0]) <= tol
+    s = scale * np.einsum("bhid,bhjd->bhij", qq, kk)
+    if causal:
+        s = np.where(np.triu(np.ones((N, N), bool), 1), -np.inf, s)
+    tot = np.exp(s - host64(lse)[..., None]).sum(-1)
+    assert np.max(np.abs(tot - 1.0)) <= 2 * TOL_LSE
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL_FWD = [
+    "bf16_b16h32n1024d64",
+    "bf16_b16h32n1024d64_causal",
+    "bf16_b4h16n4096d128_causal_x0.5",
+    "bf16_b1h16n16384d128_causal",
+    "bf16_b1h16n16384d128",
+    "bf16_b8h16n2048d128_causal_fwdbwd",
+]
+
+
+def _sample_rows(N, n, rng):
+    rows = {0, 1, N - 1, N - 2, N // 2}
+    rows.update(rng.choice(N, size=min(n, N), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+@pytest.mark.parametrize("name", FULL_FWD)
+def test_full_size_forward(fa, name):
+    """Full-size workloads in the benchmark's launch configuration, checked on
+    sampled (batch, head, row) outputs the oracle computes one by one, plus
+    output-wide properties: every element written and finite, bit-identical
+    on a repeated launch."""
+    import torch
+
+    w = fi.WORKLOADS[name]
+    x = fi.make_inputs(w, with_grad=False)
+    tq, tk, tv = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    o = torch.full_like(tq, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=tq.device)
+    st = fa.fa_forward(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       w.B, w.H, w.N, w.d, w.causal, w.scale, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    o2, lse2 = fa.forward(tq, tk, tv, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+    rng = np.random.default_rng(1)
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    oh, lh = host64(o), host64(lse)
+    worst_o = worst_l = 0.0
+    for (b, h) in sorted(heads):
+        rows = _sample_rows(w.N, 96, rng)
+        ro, rl = oracle.attention_forward_rows(fi.exact_f64(x["q"][b, h]), fi.exact_f64(x["k"][b, h]),
+                                               fi.exact_f64(x["v"][b, h]), rows, w.causal, w.scale)
+        worst_o = max(worst_o, max_abs(oh[b, h, rows], ro))
+        worst_l = max(worst_l, max_abs(lh[b, h, rows], rl))
+    assert worst_o <= TOL_BF16, worst_o
+    assert worst_l <= TOL_LSE, worst_l
+
+
+def test_full_size_backward(fa):
+    """The forward+backward workload B=8, H=16, N=2048, d=128, causal: dQ, dK,
+    dV on sampled whole heads against the oracle; whole outputs written,
+    finite and bit-identical on a repeated launch."""
+    import torch
+
+    w = fi.WORKLOADS["bf16_b8h16n2048d128_causal_fwdbwd"]
+    x = fi.make_inputs(w, with_grad=True)
+    tq, tk, tv, tdo = (dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(tq, tk, tv, causal=True, scale=w.scale)
+    grads = [torch.full_like(tq, float("nan")) for _ in range(3)]
+    ws = torch.empty(fa.fa_backward_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=tq.device)
+    st = fa.fa_backward(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        tdo.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                        w.B, w.H, w.N, w.d, 1, w.scale, ws.data_ptr(), ws.numel(),
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    again = fa.backward(tq, tk, tv, o, lse, tdo, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b in zip(grads, again):
+        assert bool(torch.isfinite(a).all())
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+    rng = np.random.default_rng(2)
+    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
+    got = [host64(t) for t in grads]
+    for (b, h) in sorted(heads):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_backward(*(fi.exact_f64(x[n][sl]) for n in ("q", "k", "v", "do")), True, w.scale)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            e = max_abs(g[sl], r)
+            assert e <= TOL_BF16, f"{name} head {(b, h)}: {e:.4g} (storage floor {storage_floor(r):.3g})"
+
+
+def test_forward_is_deterministic_across_streams(fa):
+    import torch
+
+    q, k, v = random_inputs(9, (2, 4, 777, 128), "bf16", 3)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    ref, rl = fa.forward(tq, tk, tv, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        outs = [fa.forward(tq, tk, tv, causal=True) for _ in range(5)]
+    torch.cuda.synchronize()
+    for o, lse in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+        assert torch.equal(lse, rl)
