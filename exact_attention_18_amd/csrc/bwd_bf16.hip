@@ -34,9 +34,9 @@ __device__ __forceinline__ void stage_rm(uint16_t* dst, const uint16_t* __restri
 #pragma unroll
   for (int c = tid; c < ROWS * CPR; c += NT) {
     const int row = c / CPR, col = (c % CPR) * 8;
-    uint4 x = {0, 0, 0, 0};
-    if (r0 + row < N) x = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * D + col);
-    *reinterpret_cast<uint4*>(dst + row * RS + col) = x;
+    u32x4 x = {0, 0, 0, 0};
+    if (r0 + row < N) x = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * D + col);
+    *reinterpret_cast<u32x4*>(dst + row * RS + col) = x;
   }
 }
 
@@ -50,19 +50,19 @@ __device__ __forceinline__ void stage_rm_t(uint16_t* dst_rm, uint16_t* dst_t, co
 #pragma unroll
   for (int b = tid; b < ROWS / 4 * CPR; b += NT) {
     const int rq = b / CPR, col = (b % CPR) * 8;
-    uint4 x[4];
+    u32x4 x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = r0 + 4 * rq + e;
-      x[e] = row < N ? *reinterpret_cast<const uint4*>(src + (size_t)row * D + col) : uint4{0, 0, 0, 0};
-      *reinterpret_cast<uint4*>(dst_rm + (4 * rq + e) * RS + col) = x[e];
+      x[e] = row < N ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst_rm + (4 * rq + e) * RS + col) = x[e];
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const uint32_t w0 = word_of(x[0], p), w1 = word_of(x[1], p);
       const uint32_t w2 = word_of(x[2], p), w3 = word_of(x[3], p);
-      *reinterpret_cast<uint2*>(dst_t + (col + 2 * p) * TS + 4 * rq) = uint2{lo_halves(w0, w1), lo_halves(w2, w3)};
-      *reinterpret_cast<uint2*>(dst_t + (col + 2 * p + 1) * TS + 4 * rq) = uint2{hi_halves(w0, w1), hi_halves(w2, w3)};
+      *reinterpret_cast<u32x2*>(dst_t + (col + 2 * p) * TS + 4 * rq) = u32x2{lo_halves(w0, w1), lo_halves(w2, w3)};
+      *reinterpret_cast<u32x2*>(dst_t + (col + 2 * p + 1) * TS + 4 * rq) = u32x2{hi_halves(w0, w1), hi_halves(w2, w3)};
     }
   }
 }
@@ -71,12 +71,12 @@ __device__ __forceinline__ void stage_rm_t(uint16_t* dst_rm, uint16_t* dst_t, co
 // slots (g, v) of step t mapped to columns 16t + 8(v/4) + 4g + v%4.
 __device__ __forceinline__ bf16x8 read_t_operand(const uint16_t* t_row, int col16, int g) {
   const uint16_t* p = t_row + col16 + 4 * g;
-  return bf16x8_from(*reinterpret_cast<const uint2*>(p), *reinterpret_cast<const uint2*>(p + 8));
+  return bf16x8_from(*reinterpret_cast<const u32x2*>(p), *reinterpret_cast<const u32x2*>(p + 8));
 }
 
 // Accumulator elements r = 8t .. 8t+7 of `x` as one bf16 operand.
 __device__ __forceinline__ bf16x8 acc_to_operand(const f32x16& x, int t) {
-  uint4 u = {pack_bf16x2(x[8 * t + 0], x[8 * t + 1]), pack_bf16x2(x[8 * t + 2], x[8 * t + 3]),
+  u32x4 u = {pack_bf16x2(x[8 * t + 0], x[8 * t + 1]), pack_bf16x2(x[8 * t + 2], x[8 * t + 3]),
              pack_bf16x2(x[8 * t + 4], x[8 * t + 5]), pack_bf16x2(x[8 * t + 6], x[8 * t + 7])};
   return __builtin_bit_cast(bf16x8, u);
 }
@@ -91,9 +91,9 @@ __device__ __forceinline__ void store_acc_rows(uint16_t* __restrict__ dst_row, c
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      uint2 w = {pack_bf16x2(acc[db][4 * a] * mul, acc[db][4 * a + 1] * mul),
+      u32x2 w = {pack_bf16x2(acc[db][4 * a] * mul, acc[db][4 * a + 1] * mul),
                  pack_bf16x2(acc[db][4 * a + 2] * mul, acc[db][4 * a + 3] * mul)};
-      *reinterpret_cast<uint2*>(dst_row + db * 32 + 8 * a + 4 * g) = w;
+      *reinterpret_cast<u32x2*>(dst_row + db * 32 + 8 * a + 4 * g) = w;
     }
 }
 
@@ -115,7 +115,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint16_t Gt[D * TS];
   __shared__ float lse2[Q_TILE], dl[Q_TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, g = lane >> 5;
   int bh, kb;
   map_block_xcd(blockIdx.x, total, nkb, false, bh, kb);  // causal: low key blocks carry the most work
@@ -128,10 +129,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   bf16x8 kf[KSTEPS], vf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    uint4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
     if (myk < N) {
-      a = *reinterpret_cast<const uint4*>(K + base + (size_t)myk * D + ks * 16 + 8 * g);
-      b = *reinterpret_cast<const uint4*>(V + base + (size_t)myk * D + ks * 16 + 8 * g);
+      a = *reinterpret_cast<const u32x4*>(K + base + (size_t)myk * D + ks * 16 + 8 * g);
+      b = *reinterpret_cast<const u32x4*>(V + base + (size_t)myk * D + ks * 16 + 8 * g);
     }
     kf[ks] = bf16x8_from(a);
     vf[ks] = bf16x8_from(b);
@@ -157,8 +158,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 qa = bf16x8_from(*reinterpret_cast<const uint4*>(Qs + l32 * RS + ks * 16 + 8 * g));
-        const bf16x8 ga = bf16x8_from(*reinterpret_cast<const uint4*>(Gs + l32 * RS + ks * 16 + 8 * g));
+        const bf16x8 qa = bf16x8_from(*reinterpret_cast<const u32x4*>(Qs + l32 * RS + ks * 16 + 8 * g));
+        const bf16x8 ga = bf16x8_from(*reinterpret_cast<const u32x4*>(Gs + l32 * RS + ks * 16 + 8 * g));
         s = mfma32(qa, kf[ks], s);
         dp = mfma32(ga, vf[ks], dp);
       }
@@ -205,7 +206,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[K_TILE * RS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, g = lane >> 5;
   int bh, qb;
   map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
@@ -217,10 +219,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   bf16x8 qf[KSTEPS], gf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    uint4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
     if (myq < N) {
-      a = *reinterpret_cast<const uint4*>(Q + base + (size_t)myq * D + ks * 16 + 8 * g);
-      b = *reinterpret_cast<const uint4*>(dO + base + (size_t)myq * D + ks * 16 + 8 * g);
+      a = *reinterpret_cast<const u32x4*>(Q + base + (size_t)myq * D + ks * 16 + 8 * g);
+      b = *reinterpret_cast<const u32x4*>(dO + base + (size_t)myq * D + ks * 16 + 8 * g);
     }
     qf[ks] = bf16x8_from(a);
     gf[ks] = bf16x8_from(b);
@@ -244,8 +246,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 ka = bf16x8_from(*reinterpret_cast<const uint4*>(Ks + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
-          const bf16x8 va = bf16x8_from(*reinterpret_cast<const uint4*>(Vs + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
+          const bf16x8 ka = bf16x8_from(*reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
+          const bf16x8 va = bf16x8_from(*reinterpret_cast<const u32x4*>(Vs + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
           s = mfma32(ka, qf[ks], s);
           dp = mfma32(va, gf[ks], dp);
         }

@@ -258,8 +258,8 @@ rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restric
     const T* o = O + row * d;
     const T* g = G + row * d;
     for (int col = part * EPC; col < d; col += 16 * EPC) {
-      const uint4 a = *reinterpret_cast<const uint4*>(o + col);
-      const uint4 b = *reinterpret_cast<const uint4*>(g + col);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(o + col);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(g + col);
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {

@@ -11,9 +11,24 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Native vectors for raw 16/8-byte moves (HIP's uint4/uint2 are structs,
+// which keeps some copies out of registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Multiplier taking a raw score q.k to the base-2 exponent domain:
+// scale * log2(e).  The kernels hide a masked score by setting it to -inf
+// before this multiply, which needs a strictly positive multiplier; for
+// scale = 0 a multiplier of 1e-30 is used instead, under which every exponent
+// of a finite score (|q.k| < 1e22) is below 2^-24, so exp2 returns exactly 1
+// and the weights are exactly uniform, as with scale 0.
+__host__ __device__ inline float score_coef(float scale) {
+  const float c = scale * kLog2e;
+  return c > 1e-30f ? c : 1e-30f;
+}
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -39,12 +54,51 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes at `base`: a raw buffer load whose byte
+// offset is at or past `bytes` returns zero instead of reading memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive bf16 (a row segment); lane i
+// of the group receives element i%4 of the segments of lanes i/4, i/4+4,
+// i/4+8, i/4+12.  So when lane s points at row r0 + s/4, column c0 + 4*(s%4)
+// of a row-major tile, lane i receives column c0 + i of rows r0 .. r0+3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(__attribute__((address_space(3))) uint16_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Value of x in this lane and in the lane 32 apart, via v_permlane32_swap:
+// returns {x[lane % 32], x[32 + lane % 32]}.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
 // Reassemble 8 bf16 from two 64-bit halves.
-__device__ __forceinline__ bf16x8 bf16x8_from(uint2 lo, uint2 hi) {
-  uint4 u = {lo.x, lo.y, hi.x, hi.y};
+__device__ __forceinline__ bf16x8 bf16x8_from(u32x2 lo, u32x2 hi) {
+  u32x4 u = {lo.x, lo.y, hi.x, hi.y};
   return __builtin_bit_cast(bf16x8, u);
 }
-__device__ __forceinline__ bf16x8 bf16x8_from(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 bf16x8_from(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // Byte select: result bytes picked from {hi:lo} by `sel` (v_perm_b32).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -55,9 +109,7 @@ __device__ __forceinline__ uint32_t lo_halves(uint32_t lo, uint32_t hi) { return
 // High 16-bit halves of two words: (lo.h16) | (hi.h16 << 16).
 __device__ __forceinline__ uint32_t hi_halves(uint32_t lo, uint32_t hi) { return perm_b32(hi, lo, 0x07060302u); }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
+__device__ __forceinline__ uint32_t word_of(const u32x4& u, int i) { return u[i]; }
 
 // Workgroup id -> (batch*head, query block), with
 //  * all query blocks of one (batch, head) on one XCD: the dispatcher hands

@@ -11,7 +11,9 @@
 //    is fetched into registers while tile j is computed;
 //  * S^T = K Q^T and O^T += V^T P^T on the bf16 matrix cores.  Computing the
 //    transposed products puts one query per lane (two lanes per query), so
-//    the row max, the row sum and the output rescale are per-lane values;
+//    the row max, the row sum and the output rescale are per-lane values.
+//    K and V sit in LDS row-major; the V^T operand comes from the LDS
+//    transpose read;
 //  * online softmax in the base-2 domain: scale*log2(e) is folded into one
 //    multiply-add before v_exp_f32; the running max is only raised when a
 //    tile's max exceeds it by more than 2^8 (the numerator and denominator
@@ -19,6 +21,8 @@
 //    in the epilogue;
 //  * causal: tiles above the diagonal are never loaded; the mask code runs
 //    only on tiles that straddle the diagonal or the ragged end of N.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "launch.h"
 
@@ -30,109 +34,190 @@ constexpr int BC = 64;        // keys per tile
 constexpr int NT = 256;       // threads per workgroup (4 waves)
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
 
+// Row padding (elements) of the K and V tiles in LDS; tuning knobs.
+#ifndef FA_FWD_KPAD
+#define FA_FWD_KPAD 8
+#endif
+#ifndef FA_FWD_VPAD
+#define FA_FWD_VPAD 32
+#endif
+
 template <int D>
 struct Lds {
-  static constexpr int KS = D + 8;          // K tile row stride (elements)
-  static constexpr int VS = BC + 4;         // V^T tile row stride (elements)
+  // K rows are read 16 bytes per lane from 32 consecutive rows: a row stride
+  // of D+8 elements spreads 16 consecutive rows over all 64 banks.  V rows
+  // are read with the transpose read: two 16-lane groups each take 4
+  // consecutive rows x 32 bytes; a row stride of D+32 elements (64 bytes
+  // past a multiple of 256) puts those 8 segments on disjoint banks.
+  static constexpr int KS = D + FA_FWD_KPAD;
+  static constexpr int VS = D + FA_FWD_VPAD;
   static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int ELEMS = 2 * STAGE;   // double buffer
-  static constexpr int KCH = BC * D / 8 / NT;          // 16-byte K chunks per thread
-  static constexpr int VBLK = BC / 4 * D / 8;          // 4-key x 8-column V blocks
-  static constexpr int VPT = (VBLK + NT - 1) / NT;     // V blocks per thread
+  static constexpr int STAGE = K_ELEMS + BC * VS;
+  static constexpr int ELEMS = 2 * STAGE;              // double buffer
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int CPT = BC * CPR / NT;            // chunks per thread per tensor
 };
 
 template <int D>
 struct TileRegs {
-  uint4 k[Lds<D>::KCH];
-  uint4 v[Lds<D>::VPT][4];
+  u32x4 k[Lds<D>::CPT];
+  u32x4 v[Lds<D>::CPT];
 };
 
+// Global -> registers for the tile starting at key kv0.  Buffer loads: rows
+// at or beyond N lie past the end of the buffer and read as zero.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const uint16_t* __restrict__ K,
-                                          const uint16_t* __restrict__ V, int kv0, int N, int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          int kv0, int tid) {
 #pragma unroll
-  for (int i = 0; i < Lds<D>::KCH; ++i) {
+  for (int i = 0; i < Lds<D>::CPT; ++i) {
     const int c = tid + NT * i;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    const int key = kv0 + row;
-    r.k[i] = key < N ? *reinterpret_cast<const uint4*>(K + (size_t)key * D + col) : uint4{0, 0, 0, 0};
+    const uint32_t off = (uint32_t)(((kv0 + c / Lds<D>::CPR) * D + (c % Lds<D>::CPR) * 8) * 2);
+    r.k[i] = buf_load16(kr, off);
+    r.v[i] = buf_load16(vr, off);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* stage, int tid) {
+  using L = Lds<D>;
 #pragma unroll
-  for (int i = 0; i < Lds<D>::VPT; ++i) {
-    const int b = tid + NT * i;
-    if (b < Lds<D>::VBLK) {
-      const int kq = b / CPR, col = (b % CPR) * 8;
+  for (int i = 0; i < L::CPT; ++i) {
+    const int c = tid + NT * i;
+    const int row = c / L::CPR, col = (c % L::CPR) * 8;
+    *reinterpret_cast<u32x4*>(stage + row * L::KS + col) = r.k[i];
+    *reinterpret_cast<u32x4*>(stage + L::K_ELEMS + row * L::VS + col) = r.v[i];
+  }
+}
+
+// One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax update,
+// O^T += V^T P^T.  MASK selects the variant for tiles that straddle the
+// diagonal or the end of N; `lim` is the largest visible key offset within
+// the tile for this lane's query, minus 4*g.
+template <int D, bool MASK>
+__device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&oacc)[D / 32], float& m, float& lsum, float c, int lim,
+                                          int lane) {
+  using L = Lds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // S^T tile: s[kb] element r is key 32*kb + 8*(r/4) + 4*g + r%4 of the tile.
+  // The two 32-key blocks are independent chains; alternating them keeps
+  // consecutive matrix-core instructions independent.
+  f32x16 s[2];
+  const uint16_t* krow = Ks + l32 * L::KS + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a = bf16x8_from(*reinterpret_cast<const u32x4*>(krow + kb * 32 * L::KS + ks * 16));
+      s[kb] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s[kb]);
+    }
+
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+  }
+  // Row max as a shallow tree (v_max3), not a 32-long dependent chain.
+  float m8[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h;
+      const float a = fmaxf(fmaxf(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
+      const float b = fmaxf(fmaxf(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
+      m8[2 * kb + h] = fmaxf(fmaxf(a, b), fmaxf(s[kb][r + 6], s[kb][r + 7]));
+    }
+  float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+  mx = max_halves(mx) * c;  // c > 0: the scaled row max over the tile (or -inf)
+
+  // Raise the reference max only when some row's tile max exceeds it by
+  // more than TAU; otherwise p stays below 2^TAU and nothing is rescaled.
+  if (__any(mx > m + TAU)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2_hw(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+  }
+
+  // P^T as the B operand of the PV product: accumulator elements
+  // r = 8t .. 8t+7 of block kb form contraction step (kb, t), whose slots
+  // (g, v) are keys 32kb + 16t + 4g + v (v < 4) and 32kb + 16t + 8 + 4g + v-4.
+  bf16x8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 w;
+      float ps[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = kv0 + 4 * kq + e;
-        r.v[i][e] = key < N ? *reinterpret_cast<const uint4*>(V + (size_t)key * D + col) : uint4{0, 0, 0, 0};
+        const int r = 8 * t + 2 * e;
+        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
+        ps[e] = p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);  // pairwise, shallow dependency
+      pf[kb][t] = __builtin_bit_cast(bf16x8, w);
+    }
+
+  // O^T += V^T P^T.  The V^T operand of lane l is column 32*db + l%32 of the
+  // keys of its slots, two transpose reads of 4 rows each.
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* vp = Vs + (kb * 32 + 16 * t + tr_row) * L::VS + tr_col;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 a = bf16x8_from(lds_read_tr16(vp + db * 32), lds_read_tr16(vp + 8 * L::VS + db * 32));
+        oacc[db] = mfma32(a, pf[kb][t], oacc[db]);
       }
     }
-  }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* Ks, uint16_t* Vt, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int KS = Lds<D>::KS, VS = Lds<D>::VS;
-#pragma unroll
-  for (int i = 0; i < Lds<D>::KCH; ++i) {
-    const int c = tid + NT * i;
-    const int row = c / CPR, col = (c % CPR) * 8;
-    *reinterpret_cast<uint4*>(Ks + row * KS + col) = r.k[i];
-  }
-  // V is stored transposed (column d holds 64 consecutive keys) so that the
-  // PV product can read 4 consecutive keys of one column with one 8-byte load.
-#pragma unroll
-  for (int i = 0; i < Lds<D>::VPT; ++i) {
-    const int b = tid + NT * i;
-    if (b < Lds<D>::VBLK) {
-      const int kq = b / CPR, col = (b % CPR) * 8;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = word_of(r.v[i][0], p), w1 = word_of(r.v[i][1], p);
-        const uint32_t w2 = word_of(r.v[i][2], p), w3 = word_of(r.v[i][3], p);
-        uint2 even = {lo_halves(w0, w1), lo_halves(w2, w3)};
-        uint2 odd = {hi_halves(w0, w1), hi_halves(w2, w3)};
-        *reinterpret_cast<uint2*>(Vt + (col + 2 * p) * VS + 4 * kq) = even;
-        *reinterpret_cast<uint2*>(Vt + (col + 2 * p + 1) * VS + 4 * kq) = odd;
-      }
-    }
-  }
-}
+#ifndef FA_FWD_WAVES_PER_SIMD
+#define FA_FWD_WAVES_PER_SIMD 2
+#endif
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_SIMD, FA_FWD_WAVES_PER_SIMD)))
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                 float* __restrict__ LSE, int N, int nqb, int total, float c) {
   using L = Lds<D>;
-  constexpr int KSTEPS = D / 16;   // contraction steps of S^T = K Q^T
-  constexpr int DB = D / 32;       // 32-row blocks of O^T
+  constexpr int KSTEPS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
   int bh, qb;
   map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* Kh = K + base;
-  const uint16_t* Vh = V + base;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
   const int q0 = qb * BR;
   const int qw = q0 + wave * 32;   // first query of this wave
   const int myq = qw + l32;        // query owned by this lane (with its partner lane)
 
-  // Q fragment: lane holds Q[myq][16*ks + 8*g .. +8] for every contraction step.
+  // Q fragment: lane holds Q[myq][16*ks + 8*g .. +8]; rows past N read as zero.
   bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    uint4 u = {0, 0, 0, 0};
-    if (myq < N) u = *reinterpret_cast<const uint4*>(Q + base + (size_t)myq * D + ks * 16 + 8 * g);
-    qf[ks] = bf16x8_from(u);
-  }
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    qf[ks] = bf16x8_from(buf_load16(qrs, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2)));
 
   const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -140,116 +225,42 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m = -INFINITY;   // running max of scale*log2e*s for query myq
-  float lsum = 0.f;      // this lane's share of the running row sum
+  float m = -INFINITY;   // reference max of scale*log2e*s for query myq
+  float lsum = 0.f;      // this lane's share of the row sum
 
   TileRegs<D> regs;
-  load_tile<D>(regs, Kh, Vh, 0, N, tid);
-  store_tile<D>(regs, smem, smem + L::K_ELEMS, tid);
+  load_tile<D>(regs, krs, vrs, 0, tid);
+  store_tile<D>(regs, smem, tid);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // Interior tiles (no key of the tile is hidden from any query of the
+  // workgroup) run the unmasked step; the remaining tiles (at most two on the
+  // causal diagonal, or the ragged last tile) run the masked one.  Two loops
+  // rather than a branch per tile keep the accumulators in place.
+  const int n_plain = min(CAUSAL ? q0 / BC : ntiles, N / BC);
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* Ks = smem + (j & 1) * L::STAGE;
-    const uint16_t* Vt = Ks + L::K_ELEMS;
+    const uint16_t* Vs = Ks + L::K_ELEMS;
     const int kv0 = j * BC;
-    if (j + 1 < ntiles) load_tile<D>(regs, Kh, Vh, kv0 + BC, N, tid);
-
-    if (!CAUSAL || kv0 <= qw + 31) {
-      // S^T tile: s[kb] element r is key kv0 + 32*kb + 8*(r/4) + 4*g + r%4, query myq.
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* krow = Ks + (kb * 32 + l32) * L::KS + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 a = bf16x8_from(*reinterpret_cast<const uint4*>(krow + ks * 16));
-          s[kb] = mfma32(a, qf[ks], s[kb]);
-        }
+    if (j + 1 < ntiles) load_tile<D>(regs, krs, vrs, kv0 + BC, tid);
+    if constexpr (MASK) {
+      if (!CAUSAL || kv0 <= qw + 31) {
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
+        tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
       }
-
-      const bool masked = (CAUSAL && kv0 + BC - 1 > qw) || (kv0 + BC > N);
-      float mx = -INFINITY;
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool hide = key >= N || (CAUSAL && key > myq);
-            const float t = hide ? -INFINITY : s[kb][r] * c;
-            s[kb][r] = t;
-            mx = fmaxf(mx, t);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx *= c;
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-      // Raise the reference max only when some row's tile max exceeds it by
-      // more than TAU; otherwise p stays below 2^TAU and nothing is rescaled.
-      if (__any(mx > m + TAU)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = exp2_hw(m - mn);
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      }
-
-      // P^T as the B operand of the PV product: 8 consecutive accumulator
-      // elements (r = 8t .. 8t+7) of block kb form contraction step (kb, t).
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * t + 2 * e;
-            float p0, p1;
-            if (masked) {
-              p0 = exp2_hw(s[kb][r] - m);
-              p1 = exp2_hw(s[kb][r + 1] - m);
-            } else {
-              p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
-              p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
-            }
-            w[e] = pack_bf16x2(p0, p1);
-            lsum += p0;
-            lsum += p1;
-          }
-          pf[kb][t] = __builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]});
-        }
-
-      // O^T += V^T P^T.  Slot (g, v) of step (kb, t) is key
-      // 32*kb + 16*t + 8*(v/4) + 4*g + v%4: two 8-byte reads of V^T row d.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const uint16_t* vp = Vt + (db * 32 + l32) * L::VS + kb * 32 + 16 * t + 4 * g;
-            const bf16x8 a = bf16x8_from(*reinterpret_cast<const uint2*>(vp),
-                                         *reinterpret_cast<const uint2*>(vp + 8));
-            oacc[db] = mfma32(a, pf[kb][t], oacc[db]);
-          }
-        }
+    } else {
+      tile_step<D, false>(Ks, Vs, qf, oacc, m, lsum, c, 0, lane);
     }
-
-    if (j + 1 < ntiles) store_tile<D>(regs, smem + ((j + 1) & 1) * L::STAGE,
-                                      smem + ((j + 1) & 1) * L::STAGE + L::K_ELEMS, tid);
+    if (j + 1 < ntiles) store_tile<D>(regs, smem + ((j + 1) & 1) * L::STAGE, tid);
     __syncthreads();
-  }
+  };
+  int j = 0;
+  for (; j < n_plain; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = sum_halves(lsum);
   const float inv = rcp_hw(ltot);
   if (myq < N) {
     uint16_t* orow = O + base + (size_t)myq * D;
@@ -257,9 +268,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        uint2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
+        u32x2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
                    pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
-        *reinterpret_cast<uint2*>(orow + db * 32 + 8 * a + 4 * g) = w;
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
       }
     if (g == 0) LSE[(size_t)bh * N + myq] = (m + log2_hw(ltot)) * kLn2;
   }
@@ -270,9 +281,10 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
                   int BH, int N, float scale, hipStream_t stream) {
   const int nqb = (N + BR - 1) / BR;
   const long long total = (long long)BH * nqb;
-  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+  // Buffer offsets are 32-bit: one head of K or V must stay below 2 GiB.
+  if (total > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NT), 0, stream,
-                     q, k, v, o, lse, N, nqb, (int)total, scale * kLog2e);
+                     q, k, v, o, lse, N, nqb, (int)total, score_coef(scale));
   return hipGetLastError();
 }
 
