@@ -8,15 +8,23 @@
 //     dQ = scale * dS K,   dK = scale * dS^T Q.
 // Three launches on one stream, no atomics, so the result is bit-reproducible:
 //   1. delta (row-dot pre-pass, in f32_path.hip);
-//   2. dK/dV: one workgroup per (batch*head, 128 keys), each wave owning 32
-//      keys and looping over query tiles of 32 (causal: from the diagonal on);
-//   3. dQ: one workgroup per (batch*head, 128 queries), each wave owning 32
-//      queries and looping over key tiles of 64 (causal: up to the diagonal).
+//   2. dK/dV: one workgroup per (batch*head, 128 keys); each wave owns 32
+//      keys (K rows in registers) and loops over query tiles of 32 (causal:
+//      from the diagonal on);
+//   3. dQ: one workgroup per (batch*head, 128 queries); each wave owns 32
+//      queries (Q and dO rows in registers) and loops over key tiles of 64
+//      (causal: up to the diagonal).
 // Every product runs on the 32x32x16 bf16 matrix cores.  Each kernel picks
-// the orientation (S or S^T) in which the operand it keeps in registers sits
-// on the lanes, and stages the other operands in LDS in both row-major and
-// transposed form, so every matrix-core operand is read with 8- or 16-byte
-// LDS loads.
+// the orientation (S or S^T) in which its register-resident rows sit on the
+// lanes.  Tiles stay row-major in LDS; operands that need the other
+// orientation come from the LDS transpose read.  Tiles are double-buffered:
+// tile i+1 is fetched into registers while tile i is computed.
+//
+// Ragged N needs no masks here: rows past N read as zero (buffer loads), a
+// zero key row contributes nothing to dQ, a query past N has LSE = +inf so
+// its P is 0, and results for keys or queries past N are never stored.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "launch.h"
 
@@ -25,53 +33,57 @@ namespace {
 
 constexpr int NT = 256;
 
-// Stage rows [r0, r0+ROWS) of a [N][D] bf16 matrix into LDS, row-major with
-// row stride RS elements; rows at or beyond N become zero.
-template <int ROWS, int D, int RS>
-__device__ __forceinline__ void stage_rm(uint16_t* dst, const uint16_t* __restrict__ src, int r0, int N,
-                                         int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int c = tid; c < ROWS * CPR; c += NT) {
-    const int row = c / CPR, col = (c % CPR) * 8;
-    u32x4 x = {0, 0, 0, 0};
-    if (r0 + row < N) x = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * D + col);
-    *reinterpret_cast<u32x4*>(dst + row * RS + col) = x;
-  }
-}
+// Row stride (elements) of a tile that is read both with 16-byte row reads
+// (32 rows, one column block) and with the transpose read (4 rows x 32
+// bytes per 16 lanes): 48 bytes (d=128) or 144 bytes (d=64) past a multiple
+// of 256 keeps both patterns free of bank conflicts.
+template <int D>
+constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
+// Row stride of a tile read only with 16-byte row reads.
+template <int D>
+constexpr int row_read_stride() { return D + 8; }
 
-// Stage the same rows both row-major (stride RS) and transposed (column c of
-// the tile becomes row c of `dst_t`, stride TS, so 4 consecutive source rows
-// of one column are one 8-byte word).
-template <int ROWS, int D, int RS, int TS>
-__device__ __forceinline__ void stage_rm_t(uint16_t* dst_rm, uint16_t* dst_t, const uint16_t* __restrict__ src,
-                                           int r0, int N, int tid) {
-  constexpr int CPR = D / 8;
+// Global -> register staging of ROWS x D bf16 rows starting at row r0 of a
+// buffer; rows past the buffer read as zero.
+template <int ROWS, int D>
+struct Rows {
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = ROWS * CPR / NT;
+  static_assert(CPT * NT == ROWS * CPR, "tile must split evenly over the workgroup");
+  u32x4 r[CPT];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int r0, int tid) {
 #pragma unroll
-  for (int b = tid; b < ROWS / 4 * CPR; b += NT) {
-    const int rq = b / CPR, col = (b % CPR) * 8;
-    u32x4 x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = r0 + 4 * rq + e;
-      x[e] = row < N ? *reinterpret_cast<const u32x4*>(src + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(dst_rm + (4 * rq + e) * RS + col) = x[e];
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t w0 = word_of(x[0], p), w1 = word_of(x[1], p);
-      const uint32_t w2 = word_of(x[2], p), w3 = word_of(x[3], p);
-      *reinterpret_cast<u32x2*>(dst_t + (col + 2 * p) * TS + 4 * rq) = u32x2{lo_halves(w0, w1), lo_halves(w2, w3)};
-      *reinterpret_cast<u32x2*>(dst_t + (col + 2 * p + 1) * TS + 4 * rq) = u32x2{hi_halves(w0, w1), hi_halves(w2, w3)};
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i;
+      r[i] = buf_load16(rs, (uint32_t)(((r0 + c / CPR) * D + (c % CPR) * 8) * 2));
     }
   }
+  template <int STRIDE>
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i;
+      *reinterpret_cast<u32x4*>(dst + (c / CPR) * STRIDE + (c % CPR) * 8) = r[i];
+    }
+  }
+};
+
+// Row `row` of a row-major tile, 16-byte block ks*16 + 8*g: a 32x32x16
+// operand whose rows sit on the lanes.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t* tile, int row, int ks, int g) {
+  return bf16x8_from(*reinterpret_cast<const u32x4*>(tile + row * STRIDE + ks * 16 + 8 * g));
 }
 
-// 8 bf16 MFMA-operand values of a transposed tile: row `row`, contraction
-// slots (g, v) of step t mapped to columns 16t + 8(v/4) + 4g + v%4.
-__device__ __forceinline__ bf16x8 read_t_operand(const uint16_t* t_row, int col16, int g) {
-  const uint16_t* p = t_row + col16 + 4 * g;
-  return bf16x8_from(*reinterpret_cast<const u32x2*>(p), *reinterpret_cast<const u32x2*>(p + 8));
+// Transposed operand from a row-major tile: lane l gets column col0 + l%32
+// of rows row0 + 16t + 8(v/4) + 4g + v%4 (slot v), the slot order of a
+// 32x32x16 accumulator converted with acc_to_operand(.., t).
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int row0, int col0, int t, int lane) {
+  const int g = lane >> 5;
+  const uint16_t* p = tile + (row0 + 16 * t + 4 * g + ((lane & 15) >> 2)) * STRIDE + col0 +
+                      16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return bf16x8_from(lds_read_tr16(p), lds_read_tr16(p + 8 * STRIDE));
 }
 
 // Accumulator elements r = 8t .. 8t+7 of `x` as one bf16 operand.
@@ -81,12 +93,12 @@ __device__ __forceinline__ bf16x8 acc_to_operand(const f32x16& x, int t) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Store a [D][32] accumulator set (D/32 blocks; lane holds column l%32) as
-// rows of a [N][D] bf16 matrix: element r of block db is column
-// 32*db + 8*(r/4) + 4*g + r%4 of row `row`.
+// Store a [D][32] accumulator set (lane holds column l%32) as row `dst_row`
+// of a [N][D] bf16 matrix: element r of block db is column
+// 32*db + 8*(r/4) + 4*g + r%4.
 template <int D>
-__device__ __forceinline__ void store_acc_rows(uint16_t* __restrict__ dst_row, const f32x16 (&acc)[D / 32],
-                                               float mul, int g) {
+__device__ __forceinline__ void store_acc_row(uint16_t* __restrict__ dst_row, const f32x16 (&acc)[D / 32],
+                                              float mul, int g) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -101,19 +113,28 @@ __device__ __forceinline__ void store_acc_rows(uint16_t* __restrict__ dst_row, c
 constexpr int KV_BLK = 128;   // keys per workgroup
 constexpr int Q_TILE = 32;    // queries per tile
 
+template <int D>
+struct DkdvLds {
+  static constexpr int QS = both_ways_stride<D>();   // Q and dO tiles
+  static constexpr int VS = row_read_stride<D>();    // the workgroup's V rows
+  static constexpr int TILE = Q_TILE * QS;
+  // one stage: Q tile, dO tile, then LSE*log2(e) and delta (2 x 32 floats)
+  static constexpr int STAGE = 2 * TILE + 2 * Q_TILE * 2;
+  static constexpr int V_ELEMS = KV_BLK * VS;
+  static constexpr int ELEMS = V_ELEMS + 2 * STAGE;
+};
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const float* __restrict__ LSE,
                 const uint16_t* __restrict__ dO, const float* __restrict__ delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkb, int total,
                 float c, float scale) {
-  constexpr int RS = D + 8, TS = Q_TILE + 4, KSTEPS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[Q_TILE * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[Q_TILE * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Gt[D * TS];
-  __shared__ float lse2[Q_TILE], dl[Q_TILE];
+  using L = DkdvLds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  uint16_t* Vs = smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -121,73 +142,121 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int bh, kb;
   map_block_xcd(blockIdx.x, total, nkb, false, bh, kb);  // causal: low key blocks carry the most work
   const size_t base = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
   const int k0 = kb * KV_BLK;
   const int kw = k0 + wave * 32;
   const int myk = kw + l32;
 
-  // K and V rows of this lane's key, as B operands (K^T / V^T columns).
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  // This lane's K row as the B operand of S = Q K^T (rows past N read as zero).
+  bf16x8 kf[KSTEPS];
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (myk < N) {
-      a = *reinterpret_cast<const u32x4*>(K + base + (size_t)myk * D + ks * 16 + 8 * g);
-      b = *reinterpret_cast<const u32x4*>(V + base + (size_t)myk * D + ks * 16 + 8 * g);
-    }
-    kf[ks] = bf16x8_from(a);
-    vf[ks] = bf16x8_from(b);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      kf[ks] = bf16x8_from(buf_load16(krs, (uint32_t)((myk * D + ks * 16 + 8 * g) * 2)));
   }
+  // The workgroup's V rows, staged once (B operand of dP = dO V^T).
+  {
+    Rows<KV_BLK, D> vrows;
+    vrows.load(make_rsrc(V + base, head_bytes), k0, tid);
+    vrows.template store<L::VS>(Vs, tid);
+  }
+
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dkt[i] = dvt[i] = f32x16{};
 
   const int qstart = CAUSAL ? k0 : 0;
-  for (int qt0 = qstart; qt0 < N; qt0 += Q_TILE) {
-    stage_rm_t<Q_TILE, D, RS, TS>(Qs, Qt, Q + base, qt0, N, tid);
-    stage_rm_t<Q_TILE, D, RS, TS>(Gs, Gt, dO + base, qt0, N, tid);
-    if (tid < Q_TILE) {
-      const int qi = qt0 + tid;
-      lse2[tid] = qi < N ? LSE[(size_t)bh * N + qi] * kLog2e : INFINITY;
-      dl[tid] = qi < N ? delta[(size_t)bh * N + qi] : 0.f;
-    }
-    __syncthreads();
+  const int ntiles = (N - qstart + Q_TILE - 1) / Q_TILE;
 
-    if (!CAUSAL || qt0 + Q_TILE - 1 >= kw) {
-      // S and dP with queries in registers (element r: query qt0 + 8(r/4) + 4g + r%4)
-      // and this lane's key on the lane.
-      f32x16 s = f32x16{}, dp = f32x16{};
+  // Per-tile staging: Q and dO rows, and LSE*log2(e) and delta of the tile's
+  // queries (queries past N get LSE = +inf, so their P is 0).
+  Rows<Q_TILE, D> qrows, grows;
+  uint32_t lse_bits = 0, dl_bits = 0;
+  const int qsel = tid & (Q_TILE - 1);
+  auto fetch = [&](int qt0) {
+    qrows.load(qrs, qt0, tid);
+    grows.load(grs, qt0, tid);
+    lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + qsel) * 4, 0, 0);
+    dl_bits = __builtin_amdgcn_raw_buffer_load_b32(drs, (uint32_t)(qt0 + qsel) * 4, 0, 0);
+  };
+  auto put = [&](int qt0, uint16_t* stage) {
+    qrows.template store<L::QS>(stage, tid);
+    grows.template store<L::QS>(stage + L::TILE, tid);
+    if (tid < Q_TILE) {
+      float* f = reinterpret_cast<float*>(stage + 2 * L::TILE);
+      f[tid] = qt0 + tid < N ? __uint_as_float(lse_bits) * kLog2e : INFINITY;
+      f[Q_TILE + tid] = __uint_as_float(dl_bits);
+    }
+  };
+
+  fetch(qstart);
+  put(qstart, smem + L::V_ELEMS);
+  __syncthreads();
+
+  // One query tile for this wave.  MASK: the tile may straddle the diagonal
+  // of this wave's keys (some query < some key).
+  auto step = [&](int i, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int qt0 = qstart + i * Q_TILE;
+    const uint16_t* Qs = smem + L::V_ELEMS + (i & 1) * L::STAGE;
+    const uint16_t* Gs = Qs + L::TILE;
+    const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * L::TILE);
+    const float* dls = lse2 + Q_TILE;
+    if (i + 1 < ntiles) fetch(qt0 + Q_TILE);
+
+    if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
+      // S and dP: element r is query qt0 + 8(r/4) + 4g + r%4, key myk.
+      f32x16 s, dp;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 qa = bf16x8_from(*reinterpret_cast<const u32x4*>(Qs + l32 * RS + ks * 16 + 8 * g));
-        const bf16x8 ga = bf16x8_from(*reinterpret_cast<const u32x4*>(Gs + l32 * RS + ks * 16 + 8 * g));
-        s = mfma32(qa, kf[ks], s);
-        dp = mfma32(ga, vf[ks], dp);
+        s = mfma32(row_operand<L::QS>(Qs, l32, ks, g), kf[ks], ks == 0 ? f32x16{} : s);
+        dp = mfma32(row_operand<L::QS>(Gs, l32, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
+                    ks == 0 ? f32x16{} : dp);
       }
-      const bool masked = (CAUSAL && qt0 < kw + 31) || (k0 + KV_BLK > N);
+      // hidden when key > query, i.e. query offset 8(r/4) + r%4 < lim
+      const int lim = myk - qt0 - 4 * g;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * g + (r & 3);
-        float p = exp2_hw(__builtin_fmaf(s[r], c, -lse2[qr]));
-        if (masked && (myk >= N || (CAUSAL && myk > qt0 + qr))) p = 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - dl[qr]);
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * a + 4 * g);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = 4 * a + b;
+          float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b]));
+          if (CAUSAL && MASK && 8 * a + b < lim) p = 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[b]);
+        }
       }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8 pb = acc_to_operand(s, t);
-        const bf16x8 db_ = acc_to_operand(dp, t);
+        const bf16x8 dsb = acc_to_operand(dp, t);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvt[db] = mfma32(read_t_operand(Gt + (db * 32 + l32) * TS, 16 * t, g), pb, dvt[db]);
-          dkt[db] = mfma32(read_t_operand(Qt + (db * 32 + l32) * TS, 16 * t, g), db_, dkt[db]);
+          dvt[db] = mfma32(tr_operand<L::QS>(Gs, 0, 32 * db, t, lane), pb, dvt[db]);
+          dkt[db] = mfma32(tr_operand<L::QS>(Qs, 0, 32 * db, t, lane), dsb, dkt[db]);
         }
       }
     }
+    if (i + 1 < ntiles) put(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
     __syncthreads();
-  }
+  };
+  // Causal: the first KV_BLK / Q_TILE tiles straddle the diagonals of the
+  // workgroup's waves; every later tile is fully visible.
+  int i = 0;
+  if (CAUSAL)
+    for (; i < min(ntiles, KV_BLK / Q_TILE); ++i) step(i, std::true_type{});
+  for (; i < ntiles; ++i) step(i, std::false_type{});
+
   if (myk < N) {
-    store_acc_rows<D>(dK + base + (size_t)myk * D, dkt, scale, g);
-    store_acc_rows<D>(dV + base + (size_t)myk * D, dvt, 1.0f, g);
+    store_acc_row<D>(dK + base + (size_t)myk * D, dkt, scale, g);
+    store_acc_row<D>(dV + base + (size_t)myk * D, dvt, 1.0f, g);
   }
 }
 
@@ -195,16 +264,24 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 constexpr int Q_BLK = 128;    // queries per workgroup
 constexpr int K_TILE = 64;    // keys per tile
 
+template <int D>
+struct DqLds {
+  static constexpr int KS = both_ways_stride<D>();   // K tile: row reads and transpose reads
+  static constexpr int VS = row_read_stride<D>();    // V tile: row reads
+  static constexpr int K_ELEMS = K_TILE * KS;
+  static constexpr int STAGE = K_ELEMS + K_TILE * VS;
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const float* __restrict__ LSE,
               const uint16_t* __restrict__ dO, const float* __restrict__ delta,
               uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
-  constexpr int RS = D + 8, TS = K_TILE + 4, KSTEPS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[K_TILE * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[K_TILE * RS];
+  using L = DqLds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -212,20 +289,24 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int bh, qb;
   map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
   const size_t base = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
   const int q0 = qb * Q_BLK;
   const int qw = q0 + wave * 32;
   const int myq = qw + l32;
 
+  // This lane's Q and dO rows as B operands (rows past N read as zero).
   bf16x8 qf[KSTEPS], gf[KSTEPS];
+  {
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (myq < N) {
-      a = *reinterpret_cast<const u32x4*>(Q + base + (size_t)myq * D + ks * 16 + 8 * g);
-      b = *reinterpret_cast<const u32x4*>(dO + base + (size_t)myq * D + ks * 16 + 8 * g);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const uint32_t off = (uint32_t)((myq * D + ks * 16 + 8 * g) * 2);
+      qf[ks] = bf16x8_from(buf_load16(qrs, off));
+      gf[ks] = bf16x8_from(buf_load16(grs, off));
     }
-    qf[ks] = bf16x8_from(a);
-    gf[ks] = bf16x8_from(b);
   }
   const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
   const float dlv = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
@@ -234,28 +315,39 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (int i = 0; i < DB; ++i) dqt[i] = f32x16{};
 
   const int kv_end = CAUSAL ? min(N, q0 + Q_BLK) : N;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += K_TILE) {
-    stage_rm_t<K_TILE, D, RS, TS>(Ks, Kt, K + base, kv0, N, tid);
-    stage_rm<K_TILE, D, RS>(Vs, V + base, kv0, N, tid);
-    __syncthreads();
-    if (!CAUSAL || kv0 <= qw + 31) {
-      const bool masked = (CAUSAL && kv0 + K_TILE - 1 > qw) || (kv0 + K_TILE > N);
+  const int ntiles = (kv_end + K_TILE - 1) / K_TILE;
+  Rows<K_TILE, D> krows, vrows;
+  krows.load(krs, 0, tid);
+  vrows.load(vrs, 0, tid);
+  krows.template store<L::KS>(smem, tid);
+  vrows.template store<L::VS>(smem + L::K_ELEMS, tid);
+  __syncthreads();
+
+  auto step = [&](int j, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kv0 = j * K_TILE;
+    const uint16_t* Ks = smem + (j & 1) * L::STAGE;
+    const uint16_t* Vs = Ks + L::K_ELEMS;
+    if (j + 1 < ntiles) {
+      krows.load(krs, kv0 + K_TILE, tid);
+      vrows.load(vrs, kv0 + K_TILE, tid);
+    }
+    if (!CAUSAL || !MASK || kv0 <= qw + 31) {
+      // hidden when key > myq, i.e. key offset 32kb + 8(r/4) + r%4 > lim
+      const int lim = myq - kv0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // S^T and dP^T: element r is key kv0 + 32kb + 8(r/4) + 4g + r%4, query myq.
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s, dp;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 ka = bf16x8_from(*reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
-          const bf16x8 va = bf16x8_from(*reinterpret_cast<const u32x4*>(Vs + (kb * 32 + l32) * RS + ks * 16 + 8 * g));
-          s = mfma32(ka, qf[ks], s);
-          dp = mfma32(va, gf[ks], dp);
+          s = mfma32(row_operand<L::KS>(Ks, kb * 32 + l32, ks, g), qf[ks], ks == 0 ? f32x16{} : s);
+          dp = mfma32(row_operand<L::VS>(Vs, kb * 32 + l32, ks, g), gf[ks], ks == 0 ? f32x16{} : dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           float p = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
-          if (masked && (key >= N || (CAUSAL && key > myq))) p = 0.f;
+          if (CAUSAL && MASK && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
           dp[r] = p * (dp[r] - dlv);
         }
 #pragma unroll
@@ -263,13 +355,25 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           const bf16x8 dsb = acc_to_operand(dp, t);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            dqt[db] = mfma32(read_t_operand(Kt + (db * 32 + l32) * TS, kb * 32 + 16 * t, g), dsb, dqt[db]);
+            dqt[db] = mfma32(tr_operand<L::KS>(Ks, kb * 32, 32 * db, t, lane), dsb, dqt[db]);
         }
       }
     }
+    if (j + 1 < ntiles) {
+      uint16_t* nxt = smem + ((j + 1) & 1) * L::STAGE;
+      krows.template store<L::KS>(nxt, tid);
+      vrows.template store<L::VS>(nxt + L::K_ELEMS, tid);
+    }
     __syncthreads();
-  }
-  if (myq < N) store_acc_rows<D>(dQ + base + (size_t)myq * D, dqt, scale, g);
+  };
+  // Tiles below every query's diagonal run unmasked; the last (at most two)
+  // causal tiles run masked.
+  const int n_plain = CAUSAL ? min(ntiles, q0 / K_TILE) : ntiles;
+  int j = 0;
+  for (; j < n_plain; ++j) step(j, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{});
+
+  if (myq < N) store_acc_row<D>(dQ + base + (size_t)myq * D, dqt, scale, g);
 }
 
 template <int D, bool CAUSAL>
@@ -278,9 +382,9 @@ hipError_t launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        int N, float scale, hipStream_t stream) {
   const int nkb = (N + KV_BLK - 1) / KV_BLK;
   const long long tk = (long long)BH * nkb;
-  if (tk > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (tk > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)tk), dim3(NT), 0, stream, q, k, v, lse,
-                     dO, delta, dk, dv, N, nkb, (int)tk, scale * kLog2e, scale);
+                     dO, delta, dk, dv, N, nkb, (int)tk, score_coef(scale), scale);
   return hipGetLastError();
 }
 
@@ -290,9 +394,9 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      hipStream_t stream) {
   const int nqb = (N + Q_BLK - 1) / Q_BLK;
   const long long tq = (long long)BH * nqb;
-  if (tq > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (tq > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)tq), dim3(NT), 0, stream, q, k, v, lse,
-                     dO, delta, dq, N, nqb, (int)tq, scale * kLog2e, scale);
+                     dO, delta, dq, N, nqb, (int)tq, score_coef(scale), scale);
   return hipGetLastError();
 }
 

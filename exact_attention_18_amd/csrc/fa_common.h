@@ -75,6 +75,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Maximum that propagates NaN (v_maximum_f32 / v_maximum3_f32 on gfx950).
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Value of x in this lane and in the lane 32 apart, via v_permlane32_swap:
 // returns {x[lane % 32], x[32 + lane % 32]}.
 __device__ __forceinline__ void halves(float x, float& a, float& b) {
@@ -85,7 +88,7 @@ __device__ __forceinline__ void halves(float x, float& a, float& b) {
 __device__ __forceinline__ float max_halves(float x) {
   float a, b;
   halves(x, a, b);
-  return fmaxf(a, b);
+  return max_nan(a, b);
 }
 __device__ __forceinline__ float sum_halves(float x) {
   float a, b;

@@ -123,17 +123,19 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
   }
   // Row max as a shallow tree (v_max3), not a 32-long dependent chain.
+  // max_nan (NaN-propagating maximum) lowers to v_maximum3_f32 without the
+  // operand canonicalisation that fmaxf needs in IEEE mode.
   float m8[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 8 * h;
-      const float a = fmaxf(fmaxf(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
-      const float b = fmaxf(fmaxf(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
-      m8[2 * kb + h] = fmaxf(fmaxf(a, b), fmaxf(s[kb][r + 6], s[kb][r + 7]));
+      const float a = max_nan(max_nan(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
+      const float b = max_nan(max_nan(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
+      m8[2 * kb + h] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
     }
-  float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+  float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
   mx = max_halves(mx) * c;  // c > 0: the scaled row max over the tile (or -inf)
 
   // Raise the reference max only when some row's tile max exceeds it by
