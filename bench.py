@@ -47,6 +47,52 @@ def _products(w, n):
     return f / 2 if w.causal else f
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_18_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "fa.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None if there is none for the current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(dev, mib: int, reps: int):
+    """Plain device-to-device copies of a known size, for scaling the HBM
+    byte counters: each copy reads and writes exactly `mib` MiB."""
+    import torch
+
+    src = torch.empty(mib * 2**20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(w, budget_s: float):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -89,7 +135,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-headline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 3 plain copies of MIB MiB (for counter calibration)")
+    ap.add_argument("--print-digest", action="store_true", help="print the kernel source digest and exit")
     args = ap.parse_args()
+    if args.print_digest:
+        print(kernel_source_digest())
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the attention kernels on a single "
@@ -203,6 +255,9 @@ def main():
                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
             del hq, hk, hv, ho, hl
 
+    if args.copy_calibration:
+        copy_calibration(dev, args.copy_calibration, 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -227,7 +282,8 @@ def main():
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom[0], w.name),
                      "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)},
         "kernels": kernel_table,
         "headline_forward": headline,
