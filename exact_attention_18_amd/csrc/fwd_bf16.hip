@@ -114,6 +114,16 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
       const bf16x8 a = bf16x8_from(*reinterpret_cast<const u32x4*>(krow + kb * 32 * L::KS + ks * 16));
       s[kb] = mfma32(a, qf[ks], ks == 0 ? f32x16{} : s[kb]);
     }
+  // Scheduling: keep 8 K-operand LDS reads (mask 0x100) in flight ahead of
+  // the matrix-core instructions (mask 0x008), then alternate 2 and 2.
+  constexpr int NQK = 2 * KSTEPS, AHEAD = NQK < 8 ? NQK : 8;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < (NQK - AHEAD) / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 
   if (MASK) {
 #pragma unroll
@@ -149,10 +159,10 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
     for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
   }
 
-  // P^T as the B operand of the PV product: accumulator elements
-  // r = 8t .. 8t+7 of block kb form contraction step (kb, t), whose slots
-  // (g, v) are keys 32kb + 16t + 4g + v (v < 4) and 32kb + 16t + 8 + 4g + v-4.
-  bf16x8 pf[2][2];
+  // Exponentials of block (kb, t) then its four PV products, so the matrix
+  // cores can run block b while the VALU computes block b+1.
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -167,23 +177,13 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
         ps[e] = p0 + p1;
         w[e] = pack_bf16x2(p0, p1);
       }
-      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);  // pairwise, shallow dependency
-      pf[kb][t] = __builtin_bit_cast(bf16x8, w);
-    }
-
-  // O^T += V^T P^T.  The V^T operand of lane l is column 32*db + l%32 of the
-  // keys of its slots, two transpose reads of 4 rows each.
-  const int tr_row = 4 * g + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
       const uint16_t* vp = Vs + (kb * 32 + 16 * t + tr_row) * L::VS + tr_col;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8 a = bf16x8_from(lds_read_tr16(vp + db * 32), lds_read_tr16(vp + 8 * L::VS + db * 32));
-        oacc[db] = mfma32(a, pf[kb][t], oacc[db]);
+        oacc[db] = mfma32(a, pb, oacc[db]);
       }
     }
 }
