@@ -218,6 +218,19 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dp = mfma32(row_operand<L::QS>(Gs, l32, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
                     ks == 0 ? f32x16{} : dp);
       }
+      // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
+      // matrix-core instructions (mask 0x008), then 2 products per 3 reads
+      // (deeper read-ahead does not fit the register budget at d = 128).
+      {
+        constexpr int NM = 2 * KSTEPS, NR = 3 * KSTEPS, AH = 4, STEPS = (NR - AH) / 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * STEPS, 0);
+      }
       // hidden when key > query, i.e. query offset 8(r/4) + r%4 < lim
       const int lim = myk - qt0 - 4 * g;
 #pragma unroll
@@ -242,6 +255,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           dvt[db] = mfma32(tr_operand<L::QS>(Gs, 0, 32 * db, t, lane), pb, dvt[db]);
           dkt[db] = mfma32(tr_operand<L::QS>(Qs, 0, 32 * db, t, lane), dsb, dkt[db]);
         }
+      }
+      // 4 transpose reads ahead, then one product per 2 reads.
+      {
+        constexpr int NM = 4 * DB, AH = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+        for (int u = 0; u < NM - AH / 2; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AH / 2, 0);
       }
     }
     if (i + 1 < ntiles) put(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
