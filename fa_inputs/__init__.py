@@ -32,6 +32,11 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "make_inputs",
+    "random_block_mask",
+    "local_global_block_mask",
+    "visible_pairs",
+    "BlockSparseWorkload",
+    "BLOCK_SPARSE_WORKLOADS",
 ]
 
 
@@ -141,3 +146,70 @@ def exact_f64(a: np.ndarray) -> np.ndarray:
 
 
 __all__.append("exact_f64")
+
+
+# --- block masks (block-sparse attention) ----------------------------------
+
+def random_block_mask(seed: int, nb: int, density: float) -> np.ndarray:
+    """[nb, nb] uint8 mask, each block visible with probability ``density``
+    (PCG64 seeded with (seed, 1), uniform draws in C order)."""
+    rng = np.random.default_rng([seed, 1])
+    return (rng.random((nb, nb)) < density).astype(np.uint8)
+
+
+def local_global_block_mask(nb: int, window: int, n_global: int) -> np.ndarray:
+    """[nb, nb] uint8 mask of a local band plus global blocks: query block a
+    sees key block b when |a - b| <= window, or b < n_global (global keys), or
+    a < n_global (global queries see everything)."""
+    a = np.arange(nb)[:, None]
+    b = np.arange(nb)[None, :]
+    vis = (np.abs(a - b) <= window) | (b < n_global) | (a < n_global)
+    return vis.astype(np.uint8)
+
+
+def visible_pairs(mask: np.ndarray, n: int, block: int, causal: bool) -> int:
+    """Number of (query, key) pairs a block mask leaves visible for sequence
+    length ``n`` (counted block by block; ragged last block clipped)."""
+    nb = mask.shape[0]
+    sizes = np.minimum(block, n - block * np.arange(nb))
+    total = 0
+    for a in range(nb):
+        for b in range(nb):
+            if not mask[a, b]:
+                continue
+            if not causal or b < a:
+                total += int(sizes[a]) * int(sizes[b])
+            elif b == a:
+                total += int(sizes[a]) * (int(sizes[a]) + 1) // 2
+    return total
+
+
+@dataclasses.dataclass(frozen=True)
+class BlockSparseWorkload:
+    """A block-sparse problem: a dense workload's shapes and inputs plus a
+    local-band + global-blocks mask of 128 x 128 blocks."""
+
+    base: Workload
+    window: int
+    n_global: int
+    block: int = 128
+
+    @property
+    def name(self) -> str:
+        return f"{self.base.name}_local{self.window}_global{self.n_global}"
+
+    def mask(self) -> np.ndarray:
+        nb = -(-self.base.N // self.block)
+        return local_global_block_mask(nb, self.window, self.n_global)
+
+    def fwd_flops(self) -> float:
+        w = self.base
+        return 4.0 * w.B * w.H * w.d * visible_pairs(self.mask(), w.N, self.block, w.causal)
+
+
+# 16k tokens (B x N), hidden size 2048, d = 128; 64 x 64 blocks of which a
+# band of 5 plus one global row and column are visible (about 11%).
+BLOCK_SPARSE_WORKLOADS = {
+    "bf16_b2h16n8192d128_local2_global1": BlockSparseWorkload(
+        Workload("bf16_b2h16n8192d128", "bf16", 2, 16, 8192, 128, False), window=2, n_global=1),
+}

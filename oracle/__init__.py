@@ -6,6 +6,9 @@ the benchmark's CPU-baseline leg, never by the GPU library.
 from .attention import (  # noqa: F401
     attention_backward,
     attention_forward,
+    attention_forward_block_sparse,
+    attention_forward_block_sparse_rows,
+    block_visibility,
     attention_forward_rows,
     scores,
     softmax_rows,

@@ -46,6 +46,9 @@ __all__ = [
     "attention_forward",
     "attention_forward_rows",
     "attention_backward",
+    "block_visibility",
+    "attention_forward_block_sparse",
+    "attention_forward_block_sparse_rows",
 ]
 
 
@@ -155,3 +158,64 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def block_visibility(block_mask: np.ndarray, n: int, block: int) -> np.ndarray:
+    """Element visibility [n, n] of a block mask: key j is visible to query i
+    when block_mask[i // block, j // block] is nonzero."""
+    bm = np.asarray(block_mask) != 0
+    idx = np.arange(n) // block
+    return bm[idx[:, None], idx[None, :]]
+
+
+def attention_forward_block_sparse(q, k, v, block_mask, block: int, causal: bool, scale: float):
+    """Block-sparse attention: the exact attention of the pages restricted to
+    the key blocks a caller-supplied mask marks visible.
+
+    The page "FlashAttention――GPUメモリの読み書きを減らし、注意機構を正確なまま高速・省メモリに"
+    (要約, 手法) extends FlashAttention to block-sparse attention without
+    spelling out its definition; the reading taken here: key j is visible to
+    query i iff block_mask[i // block, j // block] is nonzero (and j <= i when
+    causal); the softmax runs over the visible keys only.  A row with no
+    visible key has O = 0 and LSE = -inf.
+
+    ``block_mask`` is [ceil(N/block), ceil(N/block)], shared by every (batch,
+    head).  Returns (O, LSE) in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    vis = block_visibility(block_mask, N, block)
+    o = np.zeros((B, H, N, v.shape[-1]), dtype=np.float64)
+    lse = np.full((B, H, N), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], causal, scale)
+            s = np.where(vis, s, -np.inf)
+            live = np.isfinite(s).any(axis=1)
+            if not live.any():
+                continue
+            p, l = softmax_rows(s[live])
+            o[b, h, live] = p @ v[b, h]
+            lse[b, h, live] = l
+    return o, lse
+
+
+def attention_forward_block_sparse_rows(q_bh, k_bh, v_bh, rows, block_mask, block: int,
+                                        causal: bool, scale: float):
+    """``attention_forward_block_sparse`` for some query rows of one (batch,
+    head): the same definition evaluated for the listed rows only.  ``q_bh``
+    is [N, d]; returns (O [len(rows), d], LSE [len(rows)]); a row with no
+    visible key gets O = 0 and LSE = -inf."""
+    rows = np.asarray(rows)
+    n = np.asarray(k_bh).shape[0]
+    vis = block_visibility(block_mask, n, block)[rows]
+    s = scores(_f64(q_bh)[rows], k_bh, causal, scale, rows=rows)
+    s = np.where(vis, s, -np.inf)
+    o = np.zeros((len(rows), np.asarray(v_bh).shape[-1]), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    live = np.isfinite(s).any(axis=1)
+    if live.any():
+        p, l = softmax_rows(s[live])
+        o[live] = p @ _f64(v_bh)
+        lse[live] = l
+    return o, lse

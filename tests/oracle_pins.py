@@ -243,3 +243,92 @@ def backward_pin_failures(bwd, fwd, tol=1e-10) -> list[str]:
         if not (close(dq1, 0.0) and close(dk1, 0.0) and close(dv1, do1)):
             fails.append(f"n1:c{int(causal)}")
     return fails
+
+
+def brute_force_block_sparse(q, k, v, block_mask, block, causal, scale):
+    """Pure-Python loops: explicit visibility test, exp and normalise per row."""
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, v.shape[-1]))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                js = [j for j in range(N)
+                      if block_mask[i // block][j // block] and not (causal and j > i)]
+                if not js:
+                    continue
+                sc = [scale * sum(float(q[b, h, i, c]) * float(k[b, h, j, c]) for c in range(d)) for j in js]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                z = sum(w)
+                lse[b, h, i] = mx + math.log(z)
+                for c in range(v.shape[-1]):
+                    o[b, h, i, c] = sum(wj * float(v[b, h, j, c]) for wj, j in zip(w, js)) / z
+    return o, lse
+
+
+def block_sparse_pin_failures(bsf, dense_fwd, tol=1e-10) -> list[str]:
+    """Pins of ``bsf(q,k,v,block_mask,block,causal,scale) -> (O, LSE)``.
+
+    ``dense_fwd`` is the (separately pinned) dense forward, used where a
+    special case reduces to it."""
+    fails = []
+
+    def close(a, b, t=tol):
+        fa, fb = np.isfinite(a), np.isfinite(b)
+        if not np.array_equal(fa, fb):
+            return False
+        return np.allclose(np.where(fa, a, 0.0), np.where(fb, b, 0.0), rtol=0, atol=t) and \
+            np.array_equal(np.where(fa, 0.0, a), np.where(fb, 0.0, b))
+
+    r = _rng(31)
+    N, d, blk = 13, 3, 4          # ragged: 4 blocks, the last one holds one row
+    nb = (N + blk - 1) // blk
+    q, k, v = (r.standard_normal((2, 1, N, d)) for _ in range(3))
+    for causal in (False, True):
+        # all blocks visible: the dense attention
+        o, l = bsf(q, k, v, np.ones((nb, nb), np.uint8), blk, causal, 0.8)
+        od, ld = dense_fwd(q, k, v, causal, 0.8)
+        if not (close(o, od) and close(l, ld)):
+            fails.append(f"all_visible_is_dense:c{int(causal)}")
+        # random mask with every row keeping its diagonal block: brute force
+        bm = (r.random((nb, nb)) < 0.5).astype(np.uint8)
+        np.fill_diagonal(bm, 1)
+        bm[1, :] = 0 if not causal else bm[1, :]
+        o, l = bsf(q, k, v, bm, blk, causal, 0.8)
+        ob, lb = brute_force_block_sparse(q, k, v, bm, blk, causal, 0.8)
+        if not (close(o, ob, 1e-12) and close(l, lb, 1e-12)):
+            fails.append(f"brute_force:c{int(causal)}")
+    # lower-triangular blocks under the causal mask: the causal attention
+    tri = np.tril(np.ones((nb, nb), np.uint8))
+    o, l = bsf(q, k, v, tri, blk, True, 0.8)
+    od, ld = dense_fwd(q, k, v, True, 0.8)
+    if not (close(o, od) and close(l, ld)):
+        fails.append("lower_blocks_causal")
+    # block-diagonal mask: each diagonal block is an independent attention
+    diag = np.eye(nb, dtype=np.uint8)
+    o, l = bsf(q, k, v, diag, blk, False, 0.8)
+    ok = True
+    for bi in range(nb):
+        sl = slice(bi * blk, min(N, (bi + 1) * blk))
+        ob, lb = dense_fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], False, 0.8)
+        ok &= close(o[:, :, sl], ob) and close(l[:, :, sl], lb)
+    if not ok:
+        fails.append("block_diagonal")
+    # a row block with nothing visible: O = 0, LSE = -inf
+    empty = np.ones((nb, nb), np.uint8)
+    empty[2, :] = 0
+    o, l = bsf(q, k, v, empty, blk, False, 0.8)
+    if not (np.all(o[:, :, 8:12] == 0.0) and np.all(np.isneginf(l[:, :, 8:12]))):
+        fails.append("empty_rows")
+    # an asymmetric mask: transposing it changes the result
+    asym = np.zeros((nb, nb), np.uint8)
+    asym[:, 0] = 1
+    asym[0, :] = 1
+    asym[3, 1] = 1
+    o1, _ = bsf(q, k, v, asym, blk, False, 0.8)
+    o2, _ = bsf(q, k, v, asym.T.copy(), blk, False, 0.8)
+    ob, _ = brute_force_block_sparse(q, k, v, asym, blk, False, 0.8)
+    if not close(o1, ob, 1e-12) or close(o1, o2, 1e-6):
+        fails.append("asymmetric_mask")
+    return fails

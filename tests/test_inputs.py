@@ -1,5 +1,6 @@
 """The seeded input generators (CPU only)."""
 import numpy as np
+import pytest
 import torch
 
 import fa_inputs as fi
@@ -47,3 +48,25 @@ def test_workload_flop_counts():
     w = fi.WORKLOADS["bf16_b4h16n4096d128_causal_x0.5"]
     assert w.fwd_flops() == 4 * 4 * 16 * 4096 * 4096 * 128 / 2
     assert w.bwd_flops() == 2.5 * w.fwd_flops()
+
+
+@pytest.mark.parametrize("N", [1, 100, 128, 129, 300, 513])
+@pytest.mark.parametrize("causal", [False, True])
+def test_visible_pairs_matches_element_count(N, causal):
+    nb = -(-N // 128)
+    mask = fi.random_block_mask(3, nb, 0.5)
+    i = np.arange(N)
+    vis = mask[i[:, None] // 128, i[None, :] // 128] != 0
+    if causal:
+        vis &= i[None, :] <= i[:, None]
+    assert int(vis.sum()) == fi.visible_pairs(mask, N, 128, causal)
+
+
+def test_block_masks():
+    m = fi.local_global_block_mask(6, 1, 1)
+    assert m.dtype == np.uint8 and m.shape == (6, 6)
+    assert m[0].all() and m[:, 0].all() and m[3, 2] and m[3, 4] and not m[3, 5] and not m[5, 2]
+    a, b = fi.random_block_mask(4, 16, 0.3), fi.random_block_mask(4, 16, 0.3)
+    assert np.array_equal(a, b) and 0.1 < a.mean() < 0.5
+    w = fi.BLOCK_SPARSE_WORKLOADS["bf16_b2h16n8192d128_local2_global1"]
+    assert w.fwd_flops() == 4.0 * 2 * 16 * 128 * 128 * 128 * int(w.mask().sum())

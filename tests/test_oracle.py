@@ -53,6 +53,19 @@ def test_forward_rows_equals_full():
         assert np.array_equal(lse[0, 0, rows], lrow)
 
 
+def test_block_sparse_rows_equals_full():
+    r = np.random.default_rng(8)
+    q, k, v = (r.standard_normal((1, 1, 40, 8)) for _ in range(3))
+    mask = np.array([[1, 0, 0, 1, 0], [0, 0, 0, 0, 0], [1, 1, 0, 0, 1], [0, 1, 1, 1, 0], [1, 1, 1, 1, 1]])
+    rows = np.array([0, 3, 9, 17, 30, 39])  # row 9 sits in the empty block row
+    for causal in (False, True):
+        o, lse = oracle.attention_forward_block_sparse(q, k, v, mask, 8, causal, 0.3)
+        orow, lrow = oracle.attention_forward_block_sparse_rows(q[0, 0], k[0, 0], v[0, 0], rows, mask, 8,
+                                                                causal, 0.3)
+        assert np.array_equal(o[0, 0, rows], orow)
+        assert np.array_equal(lse[0, 0, rows], lrow)
+
+
 def test_large_scores_do_not_overflow():
     # scores near 1e3 would overflow exp() without the max subtraction
     q = np.full((1, 1, 4, 2), 30.0)
@@ -113,3 +126,22 @@ BACKWARD_MUTANTS = [
 def test_backward_pins_catch_planted_mistake(old, new):
     mutated, _ = _mutant(oa.attention_backward, old, new)
     assert pins.backward_pin_failures(mutated, oracle.attention_forward) != []
+
+
+def test_block_sparse_pins_hold():
+    assert pins.block_sparse_pin_failures(oracle.attention_forward_block_sparse, oracle.attention_forward) == []
+
+
+BLOCK_SPARSE_MUTANTS = [
+    (oa.block_visibility, "bm[idx[:, None], idx[None, :]]", "bm[idx[None, :], idx[:, None]]"),  # transposed mask
+    (oa.block_visibility, "np.arange(n) // block", "np.arange(n) // (block + 1)"),             # wrong block size
+    (oa.attention_forward_block_sparse, "s = np.where(vis, s, -np.inf)", "s = s"),             # mask ignored
+    (oa.attention_forward_block_sparse, "o = np.zeros(", "o = np.ones("),                      # empty rows not zero
+]
+
+
+@pytest.mark.parametrize("func,old,new", BLOCK_SPARSE_MUTANTS, ids=[m[2] for m in BLOCK_SPARSE_MUTANTS])
+def test_block_sparse_pins_catch_planted_mistake(func, old, new, monkeypatch):
+    mutated, _ = _mutant(func, old, new)
+    monkeypatch.setattr(oa, func.__name__, mutated)
+    assert pins.block_sparse_pin_failures(oa.attention_forward_block_sparse, oracle.attention_forward) != []
