@@ -227,7 +227,24 @@ def main():
                         "tflops": round(f / (per_kernel_ms[n] * 1e-3) / 1e12, 1) if f else None}
                     for n, _, f in kernels}
 
+    def time_launches(fn, n=10, warm=3):
+        """Mean HIP-event time (ms) of ``fn`` launched ``n`` times on ``stream``."""
+        for _ in range(warm):
+            fn()
+        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b_ in evs_:
+            a.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b_) for a, b_ in evs_]))
+
+    def checked(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {fa.fa_status_string(st)}")
+
     headline = []
+    block_sparse = []
     if not args.no_headline:
         for name in HEADLINE_FWD:
             hw = fi.WORKLOADS[name]
@@ -235,25 +252,34 @@ def main():
             hq, hk, hv = (to_dev(hx[n]) for n in ("q", "k", "v"))
             ho = torch.empty_like(hq)
             hl = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=dev)
-
-            def fwd_once():
-                st = fa.fa_forward(hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), ho.data_ptr(), hl.data_ptr(),
-                                   hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale, sp)
-                assert st == 0
-
-            for _ in range(3):
-                fwd_once()
-            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-            for a, b_ in hev:
-                a.record(stream)
-                fwd_once()
-                b_.record(stream)
-            torch.cuda.synchronize()
-            hms = float(np.mean([a.elapsed_time(b_) for a, b_ in hev]))
+            hms = time_launches(lambda: checked(fa.fa_forward(
+                hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), ho.data_ptr(), hl.data_ptr(),
+                hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale, sp), "fwd"))
             tf = hw.fwd_flops() / (hms * 1e-3) / 1e12
             headline.append({"workload": name, "kernel": "fwd", "ms": round(hms, 4), "tflops": round(tf, 1),
                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
             del hq, hk, hv, ho, hl
+
+        # Block-sparse forward: FLOPs counted on the visible (query, key)
+        # pairs only; the dense forward at the same shape is timed beside it.
+        for name, sw in fi.BLOCK_SPARSE_WORKLOADS.items():
+            bw = sw.base
+            bx = fi.make_inputs(bw, with_grad=False)
+            bq, bk, bv = (to_dev(bx[n]) for n in ("q", "k", "v"))
+            bm = torch.from_numpy(sw.mask()).to(dev)
+            bo = torch.empty_like(bq)
+            bl = torch.empty((bw.B, bw.H, bw.N), dtype=torch.float32, device=dev)
+            args_ = (bq.data_ptr(), bk.data_ptr(), bv.data_ptr(), bo.data_ptr(), bl.data_ptr())
+            sms = time_launches(lambda: checked(fa.fa_forward_block_sparse(
+                *args_, bm.data_ptr(), bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, sp), "block_sparse"))
+            dms = time_launches(lambda: checked(fa.fa_forward(
+                *args_, bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, sp), "fwd"))
+            tf = sw.fwd_flops() / (sms * 1e-3) / 1e12
+            block_sparse.append({"workload": name, "kernel": "fwd_block_sparse",
+                                 "density": round(float(sw.mask().mean()), 4), "ms": round(sms, 4),
+                                 "tflops_visible": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                 "dense_ms": round(dms, 4), "speedup_vs_dense": round(dms / sms, 2)})
+            del bq, bk, bv, bm, bo, bl
 
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
@@ -287,6 +313,7 @@ def main():
                      "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)},
         "kernels": kernel_table,
         "headline_forward": headline,
+        "block_sparse_forward": block_sparse,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

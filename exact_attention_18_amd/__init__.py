@@ -21,6 +21,7 @@ from ._lib import FA_OK, FaLibraryMissing, load  # noqa: F401
 __all__ = [
     "FaError",
     "fa_forward",
+    "fa_forward_block_sparse",
     "fa_backward",
     "fa_forward_f32",
     "fa_backward_f32",
@@ -31,8 +32,12 @@ __all__ = [
     "fa_status_string",
     "fa_abi_version",
     "forward",
+    "forward_block_sparse",
     "backward",
+    "BLOCK_SPARSE_BLOCK",
 ]
+
+BLOCK_SPARSE_BLOCK = 128  # side of a block-sparse mask block (FA_BLOCK_SPARSE_BLOCK)
 
 
 class FaError(RuntimeError):
@@ -49,6 +54,11 @@ def _call(name: str, *args) -> int:
 
 def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
     return _call("fa_forward", q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream)
+
+
+def fa_forward_block_sparse(q, k, v, o, lse, block_mask, B, H, N, d, causal, scale, stream) -> int:
+    return _call("fa_forward_block_sparse", q, k, v, o, lse, block_mask, B, H, N, d, int(causal),
+                 float(scale), stream)
 
 
 def fa_forward_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
@@ -130,6 +140,35 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None):
     fn = fa_forward_f32 if f32 else fa_forward
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
             causal, scale, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def forward_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None):
+    """Block-sparse attention (bf16): query i sees key j iff
+    ``block_mask[i // 128, j // 128]`` is nonzero (and j <= i when causal).
+
+    ``block_mask`` is a [ceil(N/128), ceil(N/128)] uint8 or bool tensor on the
+    same GPU.  Rows that see no key get o = 0 and lse = -inf.
+    """
+    import torch
+
+    _check([q, k, v], ["q", "k", "v"])
+    if q.dtype != torch.bfloat16:
+        raise TypeError("forward_block_sparse takes bfloat16 tensors")
+    B, H, N, d = q.shape
+    nb = -(-N // BLOCK_SPARSE_BLOCK)
+    if block_mask.shape != (nb, nb) or block_mask.dtype not in (torch.uint8, torch.bool):
+        raise ValueError(f"block_mask must be a uint8/bool [{nb}, {nb}] tensor")
+    if not block_mask.is_cuda or block_mask.device != q.device or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be contiguous and on the same GPU as q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 block_mask.data_ptr(), B, H, N, d, causal, scale, _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return o, lse

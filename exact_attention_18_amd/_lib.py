@@ -24,6 +24,7 @@ _sz = ctypes.c_size_t
 # name -> (restype, argtypes), in the order of include/fa.h
 SIGNATURES = {
     "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_forward_block_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                          _vp, _sz, _vp]),
     "fa_backward_preprocess": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -209,6 +209,29 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                       causal, scale, stream, true);
 }
 
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const unsigned char* block_mask, int B, int H, int N, int d, int causal,
+                            float scale, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  if (block_mask == nullptr) return FA_ERR_INVALID_ARG;
+  const size_t nb = ((size_t)N + FA_BLOCK_SPARSE_BLOCK - 1) / FA_BLOCK_SPARSE_BLOCK;
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
+  const void* inp[3] = {q, k, v};
+  const Span outs[2] = {span(o, tb), span(lse, lb)};
+  const void* outp[2] = {o, lse};
+  st = check_buffers(ins, inp, 3, outs, outp, 2);
+  if (st != FA_OK) return st;
+  const Span ms = span(block_mask, nb * nb);
+  if (overlap(ms, outs[0]) || overlap(ms, outs[1])) return FA_ERR_INVALID_ARG;
+  return hip_status(fa::launch_fwd_bf16_block_sparse(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(o), lse, block_mask, B * H, N, d, causal != 0, scale,
+      static_cast<hipStream_t>(stream)));
+}
+
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, int d, int causal, float scale, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, stream, false);

@@ -192,11 +192,16 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
 #define FA_FWD_WAVES_PER_SIMD 2
 #endif
 
-template <int D, bool CAUSAL>
+// SPARSE: block-sparse variant.  bmask is a [ceil(N/128)][ceil(N/128)] byte
+// mask shared by every (batch, head); key block kb is visible to query block
+// qb iff bmask[qb][kb] != 0 (128 x 128 blocks, so one mask row per
+// workgroup and one mask entry per two 64-key tiles).
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_SIMD, FA_FWD_WAVES_PER_SIMD)))
 fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                float* __restrict__ LSE, int N, int nqb, int total, float c) {
+                float* __restrict__ LSE, int N, int nqb, int total, float c,
+                const uint8_t* __restrict__ bmask) {
   using L = Lds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
@@ -231,6 +236,52 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float lsum = 0.f;      // this lane's share of the row sum
 
   TileRegs<D> regs;
+  if constexpr (SPARSE) {
+    // Visit only the tiles of visible key blocks and prefetch the next
+    // visible one.  A key block is two 64-key tiles.  The mask row is read
+    // 64 entries at a time into a wave-uniform bit set (one ballot).
+    // Every tile a wave visits holds key kv0 <= min(qw, N - 1), visible to
+    // all its rows, so m is finite after the wave's first tile; rows of a
+    // query block that visits no tile keep l = 0.
+    const uint8_t* mrow = bmask + (size_t)qb * nqb;
+    int win = -1;
+    uint64_t bits = 0;
+    auto first_visible_block = [&](int b) {  // smallest visible key block >= b, or nqb
+      while (b < nqb) {
+        if ((b >> 6) != win) {
+          win = b >> 6;
+          const int e = 64 * win + lane;
+          bits = __ballot(e < nqb && mrow[e] != 0);
+        }
+        const uint64_t rest = bits >> (b & 63);
+        if (rest) return b + (int)__builtin_ctzll(rest);
+        b = 64 * (win + 1);
+      }
+      return nqb;
+    };
+    int j = 2 * first_visible_block(0);
+    if (j < ntiles) {
+      load_tile<D>(regs, krs, vrs, j * BC, tid);
+      store_tile<D>(regs, smem, tid);
+    }
+    __syncthreads();
+    int slot = 0;
+    while (j < ntiles) {
+      const int jn = (j & 1) == 0 ? j + 1 : 2 * first_visible_block((j >> 1) + 1);
+      const uint16_t* Ks = smem + slot * L::STAGE;
+      const uint16_t* Vs = Ks + L::K_ELEMS;
+      const int kv0 = j * BC;
+      if (jn < ntiles) load_tile<D>(regs, krs, vrs, jn * BC, tid);
+      if (!CAUSAL || kv0 <= qw + 31) {
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
+        tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
+      }
+      if (jn < ntiles) store_tile<D>(regs, smem + (slot ^ 1) * L::STAGE, tid);
+      __syncthreads();
+      slot ^= 1;
+      j = jn;
+    }
+  } else {
   load_tile<D>(regs, krs, vrs, 0, tid);
   store_tile<D>(regs, smem, tid);
   __syncthreads();
@@ -260,10 +311,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int j = 0;
   for (; j < n_plain; ++j) step(j, std::false_type{});
   for (; j < ntiles; ++j) step(j, std::true_type{});
+  }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
+  // A row with no visible key (possible only under a block mask) gets
+  // O = 0 and LSE = -inf.
   const float ltot = sum_halves(lsum);
-  const float inv = rcp_hw(ltot);
+  const float inv = ltot > 0.f ? rcp_hw(ltot) : 0.f;
   if (myq < N) {
     uint16_t* orow = O + base + (size_t)myq * D;
 #pragma unroll
@@ -274,19 +328,19 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
       }
-    if (g == 0) LSE[(size_t)bh * N + myq] = (m + log2_hw(ltot)) * kLn2;
+    if (g == 0) LSE[(size_t)bh * N + myq] = ltot > 0.f ? (m + log2_hw(ltot)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE = false>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                  int BH, int N, float scale, hipStream_t stream) {
+                  int BH, int N, float scale, hipStream_t stream, const uint8_t* bmask = nullptr) {
   const int nqb = (N + BR - 1) / BR;
   const long long total = (long long)BH * nqb;
   // Buffer offsets are 32-bit: one head of K or V must stay below 2 GiB.
   if (total > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NT), 0, stream,
-                     q, k, v, o, lse, N, nqb, (int)total, score_coef(scale));
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)total), dim3(NT), 0, stream,
+                     q, k, v, o, lse, N, nqb, (int)total, score_coef(scale), bmask);
   return hipGetLastError();
 }
 
@@ -299,6 +353,18 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                              : launch<64, false>(q, k, v, o, lse, BH, N, scale, stream);
   if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, BH, N, scale, stream)
                               : launch<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16_block_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        uint16_t* o, float* lse, const uint8_t* block_mask, int BH,
+                                        int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch<64, true, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask)
+                  : launch<64, false, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask);
+  if (d == 128)
+    return causal ? launch<128, true, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask)
+                  : launch<128, false, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask);
   return hipErrorInvalidValue;
 }
 

@@ -13,6 +13,11 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float* lse, int BH, int N, int d, bool causal, float scale,
                            hipStream_t stream);
 
+// Block-sparse forward: block_mask is [ceil(N/128)][ceil(N/128)] bytes.
+hipError_t launch_fwd_bf16_block_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                        uint16_t* o, float* lse, const uint8_t* block_mask, int BH,
+                                        int N, int d, bool causal, float scale, hipStream_t stream);
+
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,

@@ -75,6 +75,28 @@ enum fa_status {
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, void* stream);
 
+/* Side of the square blocks of a block-sparse mask (queries and keys). */
+#define FA_BLOCK_SPARSE_BLOCK 128
+
+/*
+ * Block-sparse forward pass, bf16 in/out, float32 accumulation.  The page
+ * "FlashAttention――GPUメモリの読み書きを減らし、注意機構を正確なまま高速・省メモリに"
+ * (sections 要約 and 手法) extends FlashAttention to block-sparse attention:
+ * only the key blocks a mask marks are read and computed, the rest are
+ * skipped.  Here query i sees key j iff
+ *     block_mask[(i / 128) * nb + j / 128] != 0,   nb = ceil(N / 128),
+ * and, when causal, j <= i; the softmax runs over the visible keys only.
+ *   q, k, v, o, lse : as for fa_forward.
+ *   block_mask      : device, nb x nb bytes row-major (query block major),
+ *                     nonzero = visible, read only, any alignment; one mask
+ *                     shared by every (batch, head).
+ * A query row that sees no key gets o = 0 and lse = -inf.  With every block
+ * visible the result equals fa_forward's (same arithmetic, tile by tile).
+ */
+int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const unsigned char* block_mask, int B, int H, int N, int d,
+                            int causal, float scale, void* stream);
+
 /*
  * Backward pass, bf16 in/out, float32 accumulation: the vector-Jacobian
  * product of O with respect to Q, K and V for the incoming gradient dO.

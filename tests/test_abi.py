@@ -142,3 +142,41 @@ def test_python_binding_names_match_abi():
     for n in declared_functions():
         assert callable(getattr(fa, n)), n
     assert fa.fa_status_string(-1).startswith("FA_ERR_INVALID_ARG")
+
+
+def sparse(lib, B=1, H=1, N=300, d=64, causal=0, scale=0.125, ptrs=None):
+    p = ptrs or [ptr(i) for i in range(6)]
+    return lib.fa_forward_block_sparse(*p, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(causal=3), dict(scale=-1.0),
+                                dict(scale=math.nan), dict(B=1 << 20, H=1 << 12)])
+def test_block_sparse_rejects_bad_sizes(lib, kw):
+    assert sparse(lib, **kw) == INVALID
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_block_sparse_rejects_unsupported_head_dim(lib, d):
+    assert sparse(lib, d=d) == UNSUP
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_block_sparse_rejects_null(lib, which):
+    p = [ptr(i) for i in range(6)]
+    p[which] = None
+    assert sparse(lib, ptrs=p) == INVALID
+
+
+def test_block_sparse_mask_overlap(lib):
+    # the byte mask may sit at any address (no case here passes validation:
+    # a call that did would launch on these fake addresses), but not inside
+    # an output
+    p = [ptr(i) for i in range(6)]
+    p[5] = p[3] + 1  # mask inside o
+    assert sparse(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(6)]
+    p[5] = p[4] - 2  # mask (3 x 3 bytes for N = 300) runs into lse
+    assert sparse(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(6)]
+    p[3] = p[0] + 16  # o on q
+    assert sparse(lib, ptrs=p) == INVALID

@@ -1,0 +1,159 @@
+"""GPU parity of the block-sparse forward against the fp64 oracle.
+
+Same tolerances as the dense forward (O max-abs 2e-2, LSE 1e-3 on finite
+rows); rows that see no key must give O = 0 and LSE = -inf exactly.  With
+every block visible the block-sparse kernel must reproduce the dense forward
+bit for bit.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from tests.gpu_util import dev, host64, max_abs, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-3
+BLK = 128
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_18_amd as fa
+
+    fa._lib.load()
+    return fa
+
+
+def _mask_dev(mask):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to("cuda:0")
+
+
+def _compare(o, lse, ro, rl):
+    """O everywhere; LSE on finite rows; -inf rows exactly."""
+    oh, lh = host64(o), host64(lse)
+    assert np.all(np.isfinite(oh)), "non-finite O"
+    eo = max_abs(oh, ro)
+    assert eo <= TOL_O, f"O error {eo:.3g}"
+    dead = ~np.isfinite(rl)
+    assert np.array_equal(np.isneginf(lh), dead), "LSE -inf rows differ"
+    assert np.all(oh[dead] == 0.0), "rows with no visible key must be zero"
+    el = float(np.max(np.abs(lh[~dead] - rl[~dead]))) if (~dead).any() else 0.0
+    assert el <= TOL_LSE, f"LSE error {el:.3g}"
+
+
+def _check(fa, B, H, N, d, causal, mask, seed=0):
+    import torch
+
+    q, k, v = random_inputs(seed, (B, H, N, d), "bf16", 3)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.forward_block_sparse(dev(q), dev(k), dev(v), _mask_dev(mask), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_block_sparse(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v),
+                                                   mask, BLK, causal, scale)
+    _compare(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 65, 128, 129, 300, 1000])
+@pytest.mark.parametrize("density", [0.3, 0.7])
+def test_block_sparse_random_masks(fa, N, d, causal, density):
+    nb = -(-N // BLK)
+    mask = fi.random_block_mask(N + d, nb, density)
+    _check(fa, 2, 2, N, d, causal, mask, seed=N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_empty_rows_and_columns(fa, causal):
+    N, nb = 700, 6
+    mask = fi.random_block_mask(11, nb, 0.6)
+    mask[2, :] = 0          # query block 2 sees nothing: O = 0, LSE = -inf
+    mask[:, 4] = 0          # key block 4 is never read
+    mask[5, 5] = 1
+    _check(fa, 1, 3, N, 128, causal, mask, seed=5)
+
+
+@pytest.mark.parametrize("N", [100, 513])
+def test_block_sparse_all_hidden(fa, N):
+    import torch
+
+    nb = -(-N // BLK)
+    q, k, v = (dev(a) for a in random_inputs(3, (1, 2, N, 64), "bf16", 3))
+    o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.zeros((nb, nb), np.uint8)))
+    torch.cuda.synchronize()
+    assert bool((o.float() == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_all_visible_equals_dense_bitwise(fa, d, causal):
+    import torch
+
+    N = 777
+    nb = -(-N // BLK)
+    q, k, v = (dev(a) for a in random_inputs(4, (2, 3, N, d), "bf16", 3))
+    o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.ones((nb, nb), np.uint8)), causal=causal)
+    od, ld = fa.forward(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), od.view(torch.int16))
+    assert torch.equal(lse, ld)
+
+
+def test_block_diagonal_equals_independent_segments(fa):
+    """A block-diagonal mask is independent attention within each 128-key
+    segment: compare with the dense kernel run on each segment alone."""
+    import torch
+
+    N, nb = 512, 4
+    q, k, v = (dev(a) for a in random_inputs(6, (1, 2, N, 128), "bf16", 3))
+    o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.eye(nb, dtype=np.uint8)), causal=True)
+    for s in range(nb):
+        sl = slice(BLK * s, BLK * (s + 1))
+        os_, ls_ = fa.forward(q[:, :, sl].contiguous(), k[:, :, sl].contiguous(), v[:, :, sl].contiguous(),
+                              causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, :, sl].view(torch.int16), os_.view(torch.int16))
+        assert torch.equal(lse[:, :, sl], ls_)
+
+
+@pytest.mark.parametrize("name", sorted(fi.BLOCK_SPARSE_WORKLOADS))
+def test_full_size_block_sparse(fa, name):
+    """The benchmarked block-sparse workload at full size: sampled rows of
+    sampled heads against the oracle (restricted to those rows), whole output
+    finite, bit-identical on a repeated launch."""
+    import torch
+
+    sw = fi.BLOCK_SPARSE_WORKLOADS[name]
+    w = sw.base
+    mask = sw.mask()
+    x = fi.make_inputs(w, with_grad=False)
+    tq, tk, tv = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    tm = _mask_dev(mask)
+    o, lse = fa.forward_block_sparse(tq, tk, tv, tm, causal=w.causal, scale=w.scale)
+    o2, lse2 = fa.forward_block_sparse(tq, tk, tv, tm, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+    rng = np.random.default_rng(3)
+    oh, lh = host64(o), host64(lse)
+    for (b, h) in sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}):
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, w.N // 2, w.N - 1],
+                                         rng.choice(w.N, 48, replace=False)]))
+        ro, rl = oracle.attention_forward_block_sparse_rows(
+            fi.exact_f64(x["q"][b, h]), fi.exact_f64(x["k"][b, h]), fi.exact_f64(x["v"][b, h]), rows,
+            mask, BLK, w.causal, w.scale)
+        assert max_abs(oh[b, h, rows], ro) <= TOL_O
+        assert max_abs(lh[b, h, rows], rl) <= TOL_LSE
