@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_forward,
     attention_forward_block_sparse,
     attention_forward_block_sparse_rows,
+    attention_forward_kv,
     block_visibility,
     attention_forward_rows,
     scores,

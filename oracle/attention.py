@@ -49,6 +49,7 @@ __all__ = [
     "block_visibility",
     "attention_forward_block_sparse",
     "attention_forward_block_sparse_rows",
+    "attention_forward_kv",
 ]
 
 
@@ -218,4 +219,35 @@ def attention_forward_block_sparse_rows(q_bh, k_bh, v_bh, rows, block_mask, bloc
         p, l = softmax_rows(s[live])
         o[live] = p @ _f64(v_bh)
         lse[live] = l
+    return o, lse
+
+
+def attention_forward_kv(q, k, v, causal: bool, scale: float):
+    """Attention of Nq new queries over Nk cached keys (the decode phase).
+
+    The page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の実践的
+    エンジニアリング" (section 「実装上の差を検証可能な形で残す」) separates the prefill
+    phase from the decode phase without defining decode further; the reading
+    taken here: ``q`` [B,H,Nq,d] holds the queries of the last Nq positions
+    Nk-Nq .. Nk-1 of a sequence whose keys and values ``k``, ``v`` [B,H,Nk,d]
+    are all present.  Non-causal, every query sees every key; causal, the
+    query at position p sees keys j <= p (the square causal mask aligned at
+    the bottom right).  A query that sees no key (possible only when Nq > Nk)
+    gets O = 0 and LSE = -inf.  Returns (O [B,H,Nq,d], LSE [B,H,Nq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, nq, d = q.shape
+    nk = k.shape[2]
+    pos = np.arange(nk - nq, nk)
+    o = np.zeros((B, H, nq, v.shape[-1]), dtype=np.float64)
+    lse = np.full((B, H, nq), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = scores(q[b, h], k[b, h], causal, scale, rows=pos)
+            live = np.isfinite(s).any(axis=1)
+            if not live.any():
+                continue
+            p, l = softmax_rows(s[live])
+            o[b, h, live] = p @ v[b, h]
+            lse[b, h, live] = l
     return o, lse

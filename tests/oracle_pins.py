@@ -332,3 +332,80 @@ def block_sparse_pin_failures(bsf, dense_fwd, tol=1e-10) -> list[str]:
     if not close(o1, ob, 1e-12) or close(o1, o2, 1e-6):
         fails.append("asymmetric_mask")
     return fails
+
+
+def brute_force_kv(q, k, v, causal, scale):
+    """Pure-Python loops over queries at positions Nk-Nq+i."""
+    B, H, nq, d = q.shape
+    nk = k.shape[2]
+    o = np.zeros((B, H, nq, v.shape[-1]))
+    lse = np.full((B, H, nq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                pos = nk - nq + i
+                js = [j for j in range(nk) if not (causal and j > pos)]
+                if not js:
+                    continue
+                sc = [scale * sum(float(q[b, h, i, c]) * float(k[b, h, j, c]) for c in range(d)) for j in js]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                z = sum(w)
+                lse[b, h, i] = mx + math.log(z)
+                for c in range(v.shape[-1]):
+                    o[b, h, i, c] = sum(wj * float(v[b, h, j, c]) for wj, j in zip(w, js)) / z
+    return o, lse
+
+
+def kv_pin_failures(fkv, dense_fwd, tol=1e-10) -> list[str]:
+    """Pins of ``fkv(q, k, v, causal, scale) -> (O, LSE)`` with Nq != Nk.
+
+    ``dense_fwd`` is the (separately pinned) square forward."""
+    fails = []
+
+    def close(a, b, t=tol):
+        fa, fb = np.isfinite(a), np.isfinite(b)
+        if not np.array_equal(fa, fb):
+            return False
+        return np.allclose(np.where(fa, a, 0.0), np.where(fb, b, 0.0), rtol=0, atol=t) and \
+            np.array_equal(np.where(fa, 0.0, a), np.where(fb, 0.0, b))
+
+    r = _rng(41)
+    nk, d = 11, 3
+    qf, k, v = (r.standard_normal((2, 2, nk, d)) for _ in range(3))
+    for causal in (False, True):
+        # Nq == Nk: the square attention
+        o, l = fkv(qf, k, v, causal, 0.7)
+        od, ld = dense_fwd(qf, k, v, causal, 0.7)
+        if not (close(o, od) and close(l, ld)):
+            fails.append(f"square_is_dense:c{int(causal)}")
+        # the last Nq rows of the square attention (decode continues prefill)
+        for nq in (1, 3):
+            o, l = fkv(qf[:, :, nk - nq:], k, v, causal, 0.7)
+            if not (close(o, od[:, :, nk - nq:]) and close(l, ld[:, :, nk - nq:])):
+                fails.append(f"last_rows:c{int(causal)}:nq{nq}")
+        # brute force, a few query counts including Nq > Nk
+        for nq in (1, 4, 13):
+            qq = r.standard_normal((1, 2, nq, d))
+            o, l = fkv(qq, k[:1], v[:1], causal, 0.7)
+            ob, lb = brute_force_kv(qq, k[:1], v[:1], causal, 0.7)
+            if not (close(o, ob, 1e-12) and close(l, lb, 1e-12)):
+                fails.append(f"brute_force:c{int(causal)}:nq{nq}")
+    # one query: causal changes nothing (the last position sees every key)
+    q1 = r.standard_normal((2, 2, 1, d))
+    a, b = fkv(q1, k, v, False, 0.7), fkv(q1, k, v, True, 0.7)
+    if not (close(a[0], b[0]) and close(a[1], b[1])):
+        fails.append("one_query_causal_is_full")
+    # Q = 0: uniform weights over the visible keys
+    nq = 3
+    o, l = fkv(np.zeros((1, 1, nq, d)), k[:1, :1], v[:1, :1], True, 0.7)
+    for i in range(nq):
+        nvis = nk - nq + i + 1
+        if not (close(o[0, 0, i], v[0, 0, :nvis].mean(axis=0)) and close(l[0, 0, i], math.log(nvis))):
+            fails.append(f"zero_q_mean:{i}")
+    # more queries than keys, causal: the first Nq - Nk see nothing
+    nq = nk + 2
+    o, l = fkv(r.standard_normal((1, 1, nq, d)), k[:1, :1], v[:1, :1], True, 0.7)
+    if not (np.all(o[0, 0, :2] == 0.0) and np.all(np.isneginf(l[0, 0, :2])) and np.all(np.isfinite(l[0, 0, 2:]))):
+        fails.append("overhang_rows_empty")
+    return fails

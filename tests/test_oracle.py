@@ -145,3 +145,21 @@ def test_block_sparse_pins_catch_planted_mistake(func, old, new, monkeypatch):
     mutated, _ = _mutant(func, old, new)
     monkeypatch.setattr(oa, func.__name__, mutated)
     assert pins.block_sparse_pin_failures(oa.attention_forward_block_sparse, oracle.attention_forward) != []
+
+
+def test_kv_pins_hold():
+    assert pins.kv_pin_failures(oracle.attention_forward_kv, oracle.attention_forward) == []
+
+
+KV_MUTANTS = [
+    ("np.arange(nk - nq, nk)", "np.arange(nq)"),            # top-left instead of bottom-right causal
+    ("np.arange(nk - nq, nk)", "np.arange(nk - nq + 1, nk + 1)"),  # positions off by one
+    ("o = np.zeros(", "o = np.ones("),                       # empty rows not zero
+    ("p @ v[b, h]", "p @ v[b, h][::-1]"),                     # values reversed
+]
+
+
+@pytest.mark.parametrize("old,new", KV_MUTANTS, ids=[m[1] for m in KV_MUTANTS])
+def test_kv_pins_catch_planted_mistake(old, new):
+    mutated, _ = _mutant(oa.attention_forward_kv, old, new)
+    assert pins.kv_pin_failures(mutated, oracle.attention_forward) != []
