@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
 DEFAULT_WORKLOAD = "bf16_b8h16n2048d128_causal_fwdbwd"
 HEADLINE_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal"]
 
@@ -281,6 +282,27 @@ def main():
                                  "dense_ms": round(dms, 4), "speedup_vs_dense": round(dms / sms, 2)})
             del bq, bk, bv, bm, bo, bl
 
+    # Decode (split-KV): HBM-bound, so reported against the HBM peak with the
+    # algorithmic bytes (Q, K, V read once; O, LSE written once).
+    decode = []
+    if not args.no_headline:
+        for name, dw in fi.DECODE_WORKLOADS.items():
+            dx = fi.make_decode_inputs(dw)
+            dq_, dk_, dv_ = (to_dev(dx[n]) for n in ("q", "k", "v"))
+            do_ = torch.empty_like(dq_)
+            dl_ = torch.empty((dw.B, dw.H, dw.Nq), dtype=torch.float32, device=dev)
+            dws_bytes = fa.fa_decode_workspace_size(dw.B, dw.H, dw.Nq, dw.Nk, dw.d)
+            dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+            dms = time_launches(lambda: checked(fa.fa_decode(
+                dq_.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), do_.data_ptr(), dl_.data_ptr(), dw.B, dw.H,
+                dw.Nq, dw.Nk, dw.d, int(dw.causal), dw.scale, dws.data_ptr(), dws_bytes, sp), "decode"), n=20)
+            gbs = dw.hbm_bytes() / (dms * 1e-3) / 1e9
+            decode.append({"workload": name, "entry": "fa_decode", "ms": round(dms, 4),
+                           "algorithmic_bytes": dw.hbm_bytes(), "GB_per_s": round(gbs, 1),
+                           "hbm_peak_GB_per_s": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                           "tflops": round(dw.flops() / (dms * 1e-3) / 1e12, 2)})
+            del dq_, dk_, dv_, do_, dl_, dws
+
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
 
@@ -314,6 +336,7 @@ def main():
         "kernels": kernel_table,
         "headline_forward": headline,
         "block_sparse_forward": block_sparse,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -22,6 +22,8 @@ __all__ = [
     "FaError",
     "fa_forward",
     "fa_forward_block_sparse",
+    "fa_decode",
+    "fa_decode_workspace_size",
     "fa_backward",
     "fa_forward_f32",
     "fa_backward_f32",
@@ -33,11 +35,14 @@ __all__ = [
     "fa_abi_version",
     "forward",
     "forward_block_sparse",
+    "decode",
+    "DECODE_MAX_QUERIES",
     "backward",
     "BLOCK_SPARSE_BLOCK",
 ]
 
 BLOCK_SPARSE_BLOCK = 128  # side of a block-sparse mask block (FA_BLOCK_SPARSE_BLOCK)
+DECODE_MAX_QUERIES = 8    # FA_DECODE_MAX_QUERIES
 
 
 class FaError(RuntimeError):
@@ -59,6 +64,14 @@ def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
 def fa_forward_block_sparse(q, k, v, o, lse, block_mask, B, H, N, d, causal, scale, stream) -> int:
     return _call("fa_forward_block_sparse", q, k, v, o, lse, block_mask, B, H, N, d, int(causal),
                  float(scale), stream)
+
+
+def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_decode", q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), ws, ws_bytes, stream)
+
+
+def fa_decode_workspace_size(B, H, Nq, Nk, d) -> int:
+    return int(_call("fa_decode_workspace_size", B, H, Nq, Nk, d))
 
 
 def fa_forward_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
@@ -169,6 +182,36 @@ def forward_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     st = fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                  block_mask.data_ptr(), B, H, N, d, causal, scale, _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=None):
+    """Decode-phase attention (bf16): ``q`` [B, H, Nq, d] holds the queries of
+    the last Nq positions (1 <= Nq <= 8) of a sequence whose keys and values
+    ``k``, ``v`` are [B, H, Nk, d].  Returns (o [B, H, Nq, d], lse [B, H, Nq])."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() != 4 or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous bfloat16 [B, H, N, d] tensor on the GPU")
+        if t.device != q.device:
+            raise ValueError(f"{n} must be on the same GPU as q")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError(f"k and v must be [B, H, Nk, d] = {(B, H, Nk, d)}, got {tuple(k.shape)}, {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_size(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                   causal, scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                   _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return o, lse

@@ -25,6 +25,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_forward_block_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "fa_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                          _vp, _sz, _vp]),
     "fa_backward_preprocess": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -232,6 +232,39 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
       static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nq > FA_DECODE_MAX_QUERIES || Nk <= 0 || (d != 64 && d != 128)) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL) return 0;
+  return fa::decode_split((long long)bh, Nq, Nk, d).bytes;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+              int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Nq > FA_DECODE_MAX_QUERIES) return FA_ERR_UNSUPPORTED;
+  size_t kelems = 0, qelems = 0;
+  int st = check_common(B, H, Nk, d, causal, scale, true, &kelems);
+  if (st != FA_OK) return st;
+  st = check_common(B, H, Nq, d, causal, scale, true, &qelems);
+  if (st != FA_OK) return st;
+  if ((long long)Nk * d * 2 >= (1LL << 31)) return FA_ERR_INVALID_ARG;  // one head of K below 2 GiB
+  if ((unsigned long long)B * H * Nq > 0x7fffffffULL) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_size(B, H, Nq, Nk, d);
+  if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t qb = qelems * 2, kb = kelems * 2, lb = (size_t)B * H * Nq * sizeof(float);
+  const Span ins[3] = {span(q, qb), span(k, kb), span(v, kb)};
+  const void* inp[3] = {q, k, v};
+  const Span outs[3] = {span(o, qb), span(lse, lb), span(workspace, need)};
+  const void* outp[3] = {o, lse, workspace};
+  st = check_buffers(ins, inp, 3, outs, outp, 3);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_decode_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                           B * H, Nq, Nk, d, causal != 0, scale, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, int d, int causal, float scale, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, stream, false);

@@ -18,6 +18,20 @@ hipError_t launch_fwd_bf16_block_sparse(const uint16_t* q, const uint16_t* k, co
                                         uint16_t* o, float* lse, const uint8_t* block_mask, int BH,
                                         int N, int d, bool causal, float scale, hipStream_t stream);
 
+// Decode (1 <= nq <= 8 queries over Nk keys), split over key chunks.  The
+// workspace layout and size follow decode_split(); both the launcher and the
+// size query use it.
+struct DecodeSplit {
+  int chunk;       // keys per chunk
+  int nsplit;      // chunks per (batch, head)
+  size_t o_bytes;  // bytes of the partial outputs (256-byte multiple)
+  size_t bytes;    // total workspace bytes
+};
+DecodeSplit decode_split(long long BH, int nq, int Nk, int d);
+hipError_t launch_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                              int BH, int nq, int Nk, int d, bool causal, float scale, void* workspace,
+                              hipStream_t stream);
+
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,

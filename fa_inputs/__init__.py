@@ -37,6 +37,9 @@ __all__ = [
     "visible_pairs",
     "BlockSparseWorkload",
     "BLOCK_SPARSE_WORKLOADS",
+    "DecodeWorkload",
+    "DECODE_WORKLOADS",
+    "make_decode_inputs",
 ]
 
 
@@ -212,4 +215,57 @@ class BlockSparseWorkload:
 BLOCK_SPARSE_WORKLOADS = {
     "bf16_b2h16n8192d128_local2_global1": BlockSparseWorkload(
         Workload("bf16_b2h16n8192d128", "bf16", 2, 16, 8192, 128, False), window=2, n_global=1),
+}
+
+
+
+# --- decode (few new queries over a long key/value cache) -------------------
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new queries per (batch, head) over Nk cached keys and values."""
+
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool = True
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs per (batch, head) the mask leaves visible."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        return sum(max(0, min(self.Nk, self.Nk - self.Nq + i + 1)) for i in range(self.Nq))
+
+    def flops(self) -> float:
+        return 4.0 * self.B * self.H * self.d * self.visible_pairs()
+
+    def hbm_bytes(self) -> int:
+        """Bytes the pass must move at least: Q, K, V read once; O, LSE written."""
+        bh = self.B * self.H
+        return bh * (2 * self.Nq * self.d * 2 + 2 * self.Nk * self.d * 2 + self.Nq * 4)
+
+
+def make_decode_inputs(w: DecodeWorkload):
+    """bf16 bits of q [B,H,Nq,d], k and v [B,H,Nk,d]: PCG64(seed) standard
+    normals drawn in the order q, k, v, rounded to nearest even."""
+    rng = np.random.default_rng(w.seed)
+    out = {}
+    for n, nn in (("q", w.Nq), ("k", w.Nk), ("v", w.Nk)):
+        a = rng.standard_normal((w.B, w.H, nn, w.d), dtype=np.float32)
+        out[n] = f32_to_bf16_bits(a)
+    return out
+
+
+# A decode step of a hidden-size-2048 model (16 heads of 128) at batch 8 with
+# a 16k-token cache: 1.07 GB of keys and values per step.
+DECODE_WORKLOADS = {
+    "bf16_b8h16q1k16384d128_decode": DecodeWorkload("bf16_b8h16q1k16384d128_decode", 8, 16, 1, 16384, 128),
 }

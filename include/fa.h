@@ -23,7 +23,8 @@
  *            in float32; outputs are rounded to bf16 to nearest-even.  The _f32
  *            entry points take float32 everywhere (a slower debug path).
  * Shapes     B, H, N >= 1.  bf16: d in {64, 128}.  f32: 4 <= d <= 128 and
- *            d % 4 == 0.  Any N (a ragged last tile is masked).  N_q == N_k == N.
+ *            d % 4 == 0.  Any N (a ragged last tile is masked).  N_q == N_k == N
+ *            except for fa_decode (Nq new queries over Nk keys).
  * scale      Finite and >= 0 (0 gives uniform attention).  The caller chooses
  *            it; 1/sqrt(d) is the usual value.
  * causal     0 or 1.  1 hides key j from query i when j > i (top-left aligned).
@@ -96,6 +97,39 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                             const unsigned char* block_mask, int B, int H, int N, int d,
                             int causal, float scale, void* stream);
+
+/* Largest number of new queries per (batch, head) fa_decode accepts. */
+#define FA_DECODE_MAX_QUERIES 8
+
+/*
+ * Decode-phase forward, bf16 in/out, float32 arithmetic: Nq new queries per
+ * (batch, head) attend over Nk cached keys.  The page "Flash Attention 2で打破
+ * するローカルLLMの「メモリの壁」：IO最適化の実践的エンジニアリング" (section
+ * 「実装上の差を検証可能な形で残す」) treats the prefill and decode phases as
+ * separate workloads.  Here the queries are those of positions Nk-Nq .. Nk-1
+ * of the sequence whose keys and values are k and v; with causal = 1 the
+ * query at position p sees keys j <= p (the causal mask aligned at the bottom
+ * right), with causal = 0 every key.  A query that sees no key (Nq > Nk,
+ * causal) gets o = 0 and lse = -inf.
+ *   q        : [B][H][Nq][d] bf16, read only, 1 <= Nq <= FA_DECODE_MAX_QUERIES.
+ *   k, v     : [B][H][Nk][d] bf16, read only, Nk >= 1.
+ *   o        : [B][H][Nq][d] bf16, written.
+ *   lse      : [B][H][Nq] float32, written (natural-log row log-sum-exp).
+ *   workspace: device scratch of at least fa_decode_workspace_size() bytes,
+ *              16-byte aligned; contents on entry ignored, on return
+ *              unspecified.  It holds the per-chunk partial results: the keys
+ *              are split into chunks processed in parallel (split-KV) and
+ *              merged through their log-sum-exp.
+ * d in {64, 128}.  Deterministic (no atomics; the chunking depends only on
+ * B, H, Nq, Nk and d).
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, int causal, float scale,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_decode needs for these sizes (0 if a size is out of
+ * range).  Pure host function. */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 
 /*
  * Backward pass, bf16 in/out, float32 accumulation: the vector-Jacobian

@@ -180,3 +180,50 @@ def test_block_sparse_mask_overlap(lib):
     p = [ptr(i) for i in range(6)]
     p[3] = p[0] + 16  # o on q
     assert sparse(lib, ptrs=p) == INVALID
+
+
+def dec(lib, B=1, H=2, Nq=1, Nk=300, d=128, causal=1, scale=0.1, ptrs=None, ws_bytes=None):
+    p = ptrs or [ptr(i) for i in range(6)]
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_size(B, H, Nq, Nk, d)
+    return lib.fa_decode(*p[:5], B, H, Nq, Nk, d, causal, scale, p[5], ws_bytes, None)
+
+
+def test_decode_workspace_size(lib):
+    assert lib.fa_decode_workspace_size(1, 1, 1, 1, 64) >= 64 * 4 + 8
+    assert lib.fa_decode_workspace_size(8, 16, 1, 16384, 128) > 0
+    for bad in [(0, 1, 1, 8, 64), (1, 1, 0, 8, 64), (1, 1, 9, 8, 64), (1, 1, 1, 0, 64), (1, 1, 1, 8, 96)]:
+        assert lib.fa_decode_workspace_size(*bad) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0), dict(Nk=0), dict(causal=2), dict(scale=-1.0),
+                                dict(scale=math.inf), dict(Nk=1 << 24)])
+def test_decode_rejects_bad_sizes(lib, kw):
+    ws = None if "Nk" not in kw or kw["Nk"] > 0 else 1 << 20
+    assert dec(lib, ws_bytes=ws, **kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=9), dict(d=96), dict(d=32)])
+def test_decode_rejects_unsupported(lib, kw):
+    assert dec(lib, ws_bytes=1 << 30, **kw) == UNSUP
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_decode_rejects_null_and_misaligned(lib, which):
+    p = [ptr(i) for i in range(6)]
+    p[which] = None
+    assert dec(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(6)]
+    p[which] = ptr(which, 8)
+    assert dec(lib, ptrs=p) == INVALID
+
+
+def test_decode_rejects_overlaps_and_small_workspace(lib):
+    need = lib.fa_decode_workspace_size(1, 2, 1, 300, 128)
+    assert dec(lib, ws_bytes=need - 1) == INVALID
+    p = [ptr(i) for i in range(6)]
+    p[5] = p[3]  # workspace on o
+    assert dec(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(6)]
+    p[3] = p[1] + 256  # o inside k
+    assert dec(lib, ptrs=p) == INVALID

@@ -70,3 +70,13 @@ def test_block_masks():
     assert np.array_equal(a, b) and 0.1 < a.mean() < 0.5
     w = fi.BLOCK_SPARSE_WORKLOADS["bf16_b2h16n8192d128_local2_global1"]
     assert w.fwd_flops() == 4.0 * 2 * 16 * 128 * 128 * 128 * int(w.mask().sum())
+
+
+def test_decode_workload_counts():
+    w = fi.DecodeWorkload("t", 2, 3, 4, 10, 64, causal=True)
+    assert w.visible_pairs() == 7 + 8 + 9 + 10
+    assert fi.DecodeWorkload("t", 2, 3, 12, 10, 64, causal=True).visible_pairs() == sum(range(1, 11))
+    assert fi.DecodeWorkload("t", 2, 3, 4, 10, 64, causal=False).visible_pairs() == 40
+    x = fi.make_decode_inputs(w)
+    assert x["q"].shape == (2, 3, 4, 64) and x["k"].shape == (2, 3, 10, 64) and x["k"].dtype == np.uint16
+    assert w.hbm_bytes() == 6 * (2 * 4 * 64 * 2 + 2 * 10 * 64 * 2 + 4 * 4)
