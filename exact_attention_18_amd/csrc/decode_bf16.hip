@@ -219,7 +219,7 @@ decode_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ 
 template <int D, int NQ, bool CAUSAL>
 hipError_t launch_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* po, float* pml, int BH,
                         int nq, int Nk, int chunk, int nsplit, float scale, hipStream_t stream) {
-  constexpr int U = NQ <= 4 ? 8 : 4;
+  constexpr int U = NQ <= 2 ? 16 : NQ <= 4 ? 8 : 4;  // wave-wide loads per step (register budget)
   const long long units = (long long)BH * nsplit;
   const unsigned blocks = (unsigned)((units + DEC_WAVES - 1) / DEC_WAVES);
   hipLaunchKernelGGL((decode_split_kernel<D, NQ, U, CAUSAL>), dim3(blocks), dim3(DEC_NT), 0, stream, q, k, v,
@@ -240,10 +240,13 @@ hipError_t launch_split_nq(const uint16_t* q, const uint16_t* k, const uint16_t*
 
 DecodeSplit decode_split(long long BH, int nq, int Nk, int d) {
   // Keys per chunk: a multiple of 64 (a whole number of steps for every
-  // instantiation) sized for about 16k chunk wavefronts in all, so that even
-  // one (batch, head) fills the 256 compute units.
+  // instantiation) sized for about 2048 chunk wavefronts in all: two per SIMD,
+  // all resident at once, each streaming one long contiguous range.  Measured
+  // on MI355X, fewer longer streams beat more shorter ones (16k chunks of 128
+  // keys ran 25% slower on the B=8 H=16 Nk=16384 d=128 decode), and even one
+  // (batch, head) still fills the 256 compute units.
   DecodeSplit r;
-  const long long target = 16384;
+  const long long target = 2048;
   long long chunk = (BH * (long long)Nk + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
