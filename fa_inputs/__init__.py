@@ -40,6 +40,8 @@ __all__ = [
     "DecodeWorkload",
     "DECODE_WORKLOADS",
     "make_decode_inputs",
+    "random_signs",
+    "with_outliers",
 ]
 
 
@@ -269,3 +271,23 @@ def make_decode_inputs(w: DecodeWorkload):
 DECODE_WORKLOADS = {
     "bf16_b8h16q1k16384d128_decode": DecodeWorkload("bf16_b8h16q1k16384d128_decode", 8, 16, 1, 16384, 128),
 }
+
+
+# --- FP8 forward ----------------------------------------------------------------
+
+def random_signs(seed: int, d: int) -> np.ndarray:
+    """Length-d float32 vector of random +-1 (PCG64 seeded with (seed, 2)):
+    the random diagonal of the incoherent-processing rotation."""
+    rng = np.random.default_rng([seed, 2])
+    return (rng.integers(0, 2, size=d) * 2 - 1).astype(np.float32)
+
+
+def with_outliers(x: np.ndarray, seed: int, frac: float = 0.001, factor: float = 10.0) -> np.ndarray:
+    """Copy of float32 samples with a fraction ``frac`` of the entries (chosen
+    by PCG64 seeded with (seed, 3)) multiplied by ``factor``: the large-entry
+    outliers that incoherent processing is meant to spread."""
+    rng = np.random.default_rng([seed, 3])
+    out = np.array(x, dtype=np.float32, copy=True)
+    hit = rng.random(out.shape) < frac
+    out[hit] *= np.float32(factor)
+    return out

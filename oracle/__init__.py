@@ -14,3 +14,4 @@ from .attention import (  # noqa: F401
     scores,
     softmax_rows,
 )
+from . import fp8  # noqa: F401  (FP8 forward with incoherent processing)

@@ -409,3 +409,110 @@ def kv_pin_failures(fkv, dense_fwd, tol=1e-10) -> list[str]:
     if not (np.all(o[0, 0, :2] == 0.0) and np.all(np.isneginf(l[0, 0, :2])) and np.all(np.isfinite(l[0, 0, 2:]))):
         fails.append("overhang_rows_empty")
     return fails
+
+
+# --- FP8 forward with incoherent processing ---------------------------------
+
+def fp8_pin_failures(fp8) -> list[str]:
+    """Pins of the FP8 oracle module ``fp8`` (oracle.fp8 or a mutated copy).
+
+    Facts used: the OCP E4M3 format's fixed points (1.0 = 0x38, 448 = 0x7e,
+    2^-9 = 0x01, 2^-6 = 0x08, NaN at 0x7f), round-to-nearest-even at every
+    midpoint; the Sylvester Hadamard matrix's defining properties (H H^T = d I,
+    H_2 = [[1, 1], [1, -1]], symmetric); the butterfly equals the matrix
+    product exactly on small integers; the block exponent against a brute
+    force search; lossless round trips of representable values; FP8
+    attention on representable inputs equals exact attention; with rotation
+    the result stays near exact attention; and, as the FlashAttention-3 page
+    states, rotation lowers the FP8 error on inputs with outliers."""
+    from oracle.attention import attention_forward
+
+    fails = []
+    dec = fp8.e4m3_decode
+    fixed = {0x38: 1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0xB8: -1.0,
+             0x00: 0.0, 0x40: 2.0, 0x3C: 1.5}
+    if not all(dec(c) == v for c, v in fixed.items()) or not np.isnan(dec(0x7F)) or not np.isnan(dec(0xFF)):
+        fails.append("e4m3_fixed_points")
+    mags = dec(np.arange(0x7F))
+    if not (np.all(np.diff(mags) > 0) and np.all(np.isfinite(dec(np.arange(256))[np.r_[0:0x7F, 0x80:0xFF]]))):
+        fails.append("e4m3_monotone")
+    # every finite code round-trips; every midpoint ties to the even code
+    codes = np.r_[0:0x7F, 0x81:0xFF]
+    if not np.array_equal(fp8.e4m3_encode(dec(codes)), codes.astype(np.uint8)):
+        fails.append("e4m3_round_trip")
+    mid = 0.5 * (mags[:-1] + mags[1:])
+    want = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F))
+    if not np.array_equal(fp8.e4m3_encode(mid), want.astype(np.uint8)):
+        fails.append("e4m3_ties_to_even")
+    up, down = np.nextafter(mid, np.inf), np.nextafter(mid, -np.inf)
+    if not (np.array_equal(fp8.e4m3_encode(up), np.arange(1, 0x7F).astype(np.uint8))
+            and np.array_equal(fp8.e4m3_encode(down), np.arange(0x7E).astype(np.uint8))):
+        fails.append("e4m3_nearest")
+    if not (fp8.e4m3_encode(460.0) == 0x7E and fp8.e4m3_encode(464.0) == 0x7E and fp8.e4m3_encode(-2.0 ** -10) == 0x80
+            and fp8.e4m3_encode(-0.0) == 0x80):
+        fails.append("e4m3_edges")
+
+    # Hadamard matrix and the butterfly
+    h2 = fp8.hadamard_matrix(2)
+    h = fp8.hadamard_matrix(128)
+    if not (np.array_equal(h2, [[1, 1], [1, -1]]) and np.array_equal(h @ h.T, 128 * np.eye(128))
+            and np.array_equal(h, h.T) and set(np.unique(h)) == {-1.0, 1.0}):
+        fails.append("hadamard_matrix")
+    r = _rng(51)
+    xi = r.integers(-20, 21, size=(5, 128)).astype(np.float32)
+    if not np.array_equal(fp8.fwht_f32(xi), (xi.astype(np.float64) @ h).astype(np.float32)):
+        fails.append("fwht_exact_on_integers")
+    xf = r.standard_normal((7, 64)).astype(np.float32)
+    if not np.allclose(fp8.fwht_f32(xf), xf.astype(np.float64) @ fp8.hadamard_matrix(64), rtol=0, atol=1e-4):
+        fails.append("fwht_close")
+
+    # block exponent: smallest t with amax <= 448 * 2^t
+    amax = np.concatenate([r.random(200) * 10.0 ** r.integers(-8, 8, 200),
+                           448.0 * 2.0 ** np.arange(-10, 10), np.nextafter(448.0 * 2.0 ** np.arange(-10, 10), np.inf)])
+    brute = np.array([min(t for t in range(-200, 200) if a <= 448.0 * 2.0 ** t) for a in amax])
+    if not np.array_equal(fp8.block_exponent(amax), brute) or fp8.block_exponent(0.0) != 0:
+        fails.append("block_exponent")
+
+    # quantisation: representable values are lossless; others within half an ulp (2^-4 relative)
+    rep = (r.integers(-15, 16, size=(2, 3, 40, 128)) * 2.0 ** r.integers(-3, 4, size=(2, 3, 40, 1))).astype(np.float32)
+    c, t = fp8.quantize_rows(rep)
+    back = (fp8.e4m3_decode(c).reshape(2, 3, 40, 4, 32) * np.exp2(t)[..., None]).reshape(rep.shape)
+    if not np.array_equal(back, rep):
+        fails.append("quantize_rows_lossless")
+    x = r.standard_normal((3, 200, 64)).astype(np.float32)
+    c, t = fp8.quantize_rows(x)
+    back = (fp8.e4m3_decode(c).reshape(3, 200, 2, 32) * np.exp2(t)[..., None]).reshape(x.shape)
+    tb = np.repeat(np.exp2(t), 32, axis=-1)
+    if not np.all(np.abs(back - x) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * tb)):
+        fails.append("quantize_rows_half_ulp")
+    if not np.array_equal(np.sort(fp8.v_tile_groups().ravel()), np.arange(64)):
+        fails.append("v_groups_partition")
+
+    # attention on representable inputs (no rotation) is exact attention
+    N, d = 70, 64   # ragged: two 64-key tiles, the second holding 6 keys
+    qv = [(r.integers(-6, 7, size=(1, 2, N, d)) * 0.25) for _ in range(3)]
+    o, l = fp8.attention_forward_fp8(*qv, None, True, 0.3)
+    od, ld = attention_forward(*qv, True, 0.3)
+    if not (np.allclose(o, od, rtol=0, atol=1e-12) and np.allclose(l, ld, rtol=0, atol=1e-12)):
+        fails.append("representable_is_exact")
+    # rotation keeps Q K^T: the rotated FP8 result stays near exact attention
+    sg = np.where(r.random(d) < 0.5, -1.0, 1.0)
+    qn = [r.standard_normal((1, 2, N, d)) for _ in range(3)]
+    o, l = fp8.attention_forward_fp8(*qn, sg, False, 1 / 8)
+    od, ld = attention_forward(*qn, False, 1 / 8)
+    # (FP8 keeps about 4 significant bits: errors near 0.07 are expected, a
+    # broken rotation gives errors of order 1)
+    if not (np.abs(o - od).max() < 0.25 and np.abs(l - ld).max() < 0.15):
+        fails.append("rotated_near_exact")
+    # the page's claim: rotation lowers the error when Q and K have outliers
+    d = 128
+    qo, ko, vo = (r.standard_normal((1, 2, 256, d)) for _ in range(3))
+    for a in (qo, ko):
+        a[r.random(a.shape) < 0.001] *= 10.0
+    sg = np.where(r.random(d) < 0.5, -1.0, 1.0)
+    ref, _ = attention_forward(qo, ko, vo, False, d ** -0.5)
+    e_plain = np.sqrt(np.mean((fp8.attention_forward_fp8(qo, ko, vo, None, False, d ** -0.5)[0] - ref) ** 2))
+    e_rot = np.sqrt(np.mean((fp8.attention_forward_fp8(qo, ko, vo, sg, False, d ** -0.5)[0] - ref) ** 2))
+    if not e_rot * 1.5 < e_plain:
+        fails.append("rotation_lowers_outlier_error")
+    return fails

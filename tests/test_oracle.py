@@ -163,3 +163,39 @@ KV_MUTANTS = [
 def test_kv_pins_catch_planted_mistake(old, new):
     mutated, _ = _mutant(oa.attention_forward_kv, old, new)
     assert pins.kv_pin_failures(mutated, oracle.attention_forward) != []
+
+
+def test_fp8_pins_hold():
+    from oracle import fp8
+    assert pins.fp8_pin_failures(fp8) == []
+
+
+FP8_MUTANTS = [
+    ("fwht_f32", "np.stack([a + b, a - b]", "np.stack([a + b, b - a]"),              # wrong butterfly sign
+    ("block_exponent", "e - 9, e - 8", "e - 8, e - 8"),                              # exponent off by one
+    ("e4m3_encode", "(_MAG_CODES[i] & 1) == 0", "(_MAG_CODES[i] & 1) == 1"),          # ties to odd
+    ("attention_forward_fp8", "s_scale = float(scale) / d", "s_scale = float(scale)"),  # rotation scale lost
+    ("attention_forward_fp8", "kr = fwht_f32(k.astype(np.float32) * sg)",
+     "kr = fwht_f32(k.astype(np.float32))"),                                          # K rotated without signs
+    ("_dequant_v", "tiles[..., v_tile_groups(), :] = grp",
+     "tiles[..., v_tile_groups()[::-1], :] = grp"),                                    # V values at the wrong keys
+    ("e4m3_decode", "(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),                            # wrong mantissa width
+]
+
+
+@pytest.mark.parametrize("func,old,new", FP8_MUTANTS, ids=[m[2] for m in FP8_MUTANTS])
+def test_fp8_pins_catch_planted_mistake(func, old, new):
+    import types
+
+    from oracle import fp8
+    src = inspect.getsource(fp8)
+    assert old in src, (func, old)
+    mod = types.ModuleType("fp8_mutant")
+    mod.__dict__["__name__"] = "oracle.fp8_mutant"
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), "<fp8 mutant>", "exec"), mod.__dict__)
+    try:
+        fails = pins.fp8_pin_failures(mod)
+    except Exception as e:  # a mutant that breaks a shape or a range also counts as caught
+        fails = [repr(e)]
+    assert fails != []
