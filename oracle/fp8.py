@@ -25,10 +25,8 @@ What it computes, and where that is described:
     (a, b) becomes (a + b, a - b)); the 1/sqrt(d) of both Q and K is folded
     into the softmax scale as 1/d.
   - Scales are powers of two, one per block of 32 consecutive elements (of a
-    row of Q or K; of a column of V over 32 keys), the smallest 2^t with
-    amax <= 448 * 2^t, so no value saturates.  V's key groups of 32 are, in
-    each tile of 64 keys, the keys whose index bit 2 is equal (keys 0-3,
-    8-11, ..., 56-59 and 4-7, 12-15, ..., 60-63 of the tile).
+    row of Q or K; of a column of V over 32 consecutive keys), the smallest
+    2^t with amax <= 448 * 2^t, so no value saturates.
   - The attention itself is then exact (float64) on the dequantised values.
     The kernel also rounds P to FP8 before the P V product; that rounding is
     not modelled here, and the tests bound its effect (``p_error_bound``).
@@ -51,7 +49,6 @@ __all__ = [
     "block_exponent",
     "quantize_rows",
     "quantize_v",
-    "v_tile_groups",
     "attention_forward_fp8",
 ]
 
@@ -134,28 +131,17 @@ def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
     return codes.reshape(x.shape), t
 
 
-def v_tile_groups() -> np.ndarray:
-    """[2, 32] key offsets within a 64-key tile of V's two quantisation
-    groups, in the order their codes are stored (group g holds the keys whose
-    bit 2 equals g)."""
-    keys = np.arange(V_TILE)
-    return np.stack([keys[((keys >> 2) & 1) == g] for g in (0, 1)])
-
-
 def quantize_v(v) -> tuple[np.ndarray, np.ndarray]:
-    """Codes and exponents of V [..., N, d] in groups of 32 keys per column:
-    returns codes [..., T, d, 2, 32] and exponents [..., T, 2, d] where T is
-    the number of 64-key tiles (keys past N are zero)."""
+    """Codes and exponents of V [..., N, d] in blocks of 32 consecutive keys
+    per column: returns codes [..., d, Np] (V transposed, keys in order,
+    Np = N rounded up to a multiple of 64, keys past N zero) and exponents
+    [..., d, Np/32]."""
     v = np.asarray(v, dtype=np.float64)
     n, d = v.shape[-2:]
-    nt = -(-n // V_TILE)
-    pad = np.zeros((*v.shape[:-2], nt * V_TILE, d))
-    pad[..., :n, :] = v
-    tiles = pad.reshape(*v.shape[:-2], nt, V_TILE, d)
-    grp = tiles[..., v_tile_groups(), :]                # [..., T, 2, 32, d]
-    t = block_exponent(np.abs(grp).max(axis=-2))       # [..., T, 2, d]
-    codes = e4m3_encode(grp * np.exp2(-t.astype(np.float64))[..., None, :])
-    return np.moveaxis(codes, -1, -3), t                # [..., T, d, 2, 32]
+    np_ = -(-n // V_TILE) * V_TILE
+    vt = np.zeros((*v.shape[:-2], d, np_), dtype=np.float32)
+    vt[..., :n] = np.swapaxes(v, -1, -2)
+    return quantize_rows(vt)
 
 
 def _dequant_rows(codes, t):
@@ -165,14 +151,7 @@ def _dequant_rows(codes, t):
 
 
 def _dequant_v(codes, t, n):
-    vals = e4m3_decode(codes)                          # [..., T, d, 2, 32]
-    vals = vals * np.exp2(np.moveaxis(t, -1, -2).astype(np.float64))[..., None]   # t -> [..., T, d, 2]
-    grp = np.moveaxis(vals, -3, -1)                     # [..., T, 2, 32, d]
-    nt = grp.shape[-4]
-    d = grp.shape[-1]
-    tiles = np.zeros((*grp.shape[:-4], nt, V_TILE, d))
-    tiles[..., v_tile_groups(), :] = grp
-    return tiles.reshape(*grp.shape[:-4], nt * V_TILE, d)[..., :n, :]
+    return np.swapaxes(_dequant_rows(codes, t), -1, -2)[..., :n, :]
 
 
 def attention_forward_fp8(q, k, v, signs, causal: bool, scale: float, return_parts: bool = False):

@@ -177,8 +177,8 @@ FP8_MUTANTS = [
     ("attention_forward_fp8", "s_scale = float(scale) / d", "s_scale = float(scale)"),  # rotation scale lost
     ("attention_forward_fp8", "kr = fwht_f32(k.astype(np.float32) * sg)",
      "kr = fwht_f32(k.astype(np.float32))"),                                          # K rotated without signs
-    ("_dequant_v", "tiles[..., v_tile_groups(), :] = grp",
-     "tiles[..., v_tile_groups()[::-1], :] = grp"),                                    # V values at the wrong keys
+    ("_dequant_v", "np.swapaxes(_dequant_rows(codes, t), -1, -2)[..., :n, :]",
+     "_dequant_rows(codes, t)[..., :n]"),                                              # V used untransposed
     ("e4m3_decode", "(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),                            # wrong mantissa width
 ]
 
