@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
+PEAK_FP8_TFLOPS = 5033.2   # dense FP8 matrix cores, twice the bf16 rate
 DEFAULT_WORKLOAD = "bf16_b8h16n2048d128_causal_fwdbwd"
 HEADLINE_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal"]
 
@@ -282,6 +283,33 @@ def main():
                                  "dense_ms": round(dms, 4), "speedup_vs_dense": round(dms / sms, 2)})
             del bq, bk, bv, bm, bo, bl
 
+    # FP8 forward with incoherent processing on the headline shapes: the
+    # quantisation pass and the attention are timed apart; the attention's
+    # rate is set against the dense FP8 matrix-core peak.
+    fp8 = []
+    if not args.no_headline:
+        signs = torch.from_numpy(fi.random_signs(0, 128)).to(dev)
+        for name in HEADLINE_FWD:
+            hw = fi.WORKLOADS[name]
+            hx = fi.make_inputs(hw, with_grad=False)
+            hq, hk, hv = (to_dev(hx[n]) for n in ("q", "k", "v"))
+            ho = torch.empty_like(hq)
+            hl = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=dev)
+            nb = fa.fa_fp8_buffer_size(hw.B, hw.H, hw.N, hw.d)
+            hb = torch.empty(nb, dtype=torch.uint8, device=dev)
+            pms = time_launches(lambda: checked(fa.fa_fp8_prepare(
+                hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), signs.data_ptr(), hw.B, hw.H, hw.N, hw.d,
+                hb.data_ptr(), nb, sp), "fp8_prepare"))
+            fms = time_launches(lambda: checked(fa.fa_forward_fp8_prepared(
+                hb.data_ptr(), nb, ho.data_ptr(), hl.data_ptr(), hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale,
+                1, sp), "fp8_forward"))
+            tf = hw.fwd_flops() / (fms * 1e-3) / 1e12
+            fp8.append({"workload": name, "kernel": "fwd_fp8", "prepare_ms": round(pms, 4), "ms": round(fms, 4),
+                        "tflops": round(tf, 1), "peak_fp8": PEAK_FP8_TFLOPS,
+                        "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                        "tflops_incl_prepare": round(hw.fwd_flops() / ((fms + pms) * 1e-3) / 1e12, 1)})
+            del hq, hk, hv, ho, hl, hb
+
     # Decode (split-KV): HBM-bound, so reported against the HBM peak with the
     # algorithmic bytes (Q, K, V read once; O, LSE written once).
     decode = []
@@ -337,6 +365,7 @@ def main():
         "headline_forward": headline,
         "block_sparse_forward": block_sparse,
         "decode": decode,
+        "fp8_forward": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -23,6 +23,10 @@ __all__ = [
     "fa_forward",
     "fa_forward_block_sparse",
     "fa_decode",
+    "fa_fp8_buffer_size",
+    "fa_fp8_prepare",
+    "fa_forward_fp8_prepared",
+    "fa_forward_fp8",
     "fa_decode_workspace_size",
     "fa_backward",
     "fa_forward_f32",
@@ -36,6 +40,8 @@ __all__ = [
     "forward",
     "forward_block_sparse",
     "decode",
+    "prepare_fp8",
+    "forward_fp8",
     "DECODE_MAX_QUERIES",
     "backward",
     "BLOCK_SPARSE_BLOCK",
@@ -72,6 +78,24 @@ def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ws, ws_bytes, str
 
 def fa_decode_workspace_size(B, H, Nq, Nk, d) -> int:
     return int(_call("fa_decode_workspace_size", B, H, Nq, Nk, d))
+
+
+def fa_fp8_buffer_size(B, H, N, d) -> int:
+    return int(_call("fa_fp8_buffer_size", B, H, N, d))
+
+
+def fa_fp8_prepare(q, k, v, signs, B, H, N, d, buf, buf_bytes, stream) -> int:
+    return _call("fa_fp8_prepare", q, k, v, signs, B, H, N, d, buf, buf_bytes, stream)
+
+
+def fa_forward_fp8_prepared(buf, buf_bytes, o, lse, B, H, N, d, causal, scale, rotated, stream) -> int:
+    return _call("fa_forward_fp8_prepared", buf, buf_bytes, o, lse, B, H, N, d, int(causal), float(scale),
+                 int(rotated), stream)
+
+
+def fa_forward_fp8(q, k, v, signs, o, lse, B, H, N, d, causal, scale, buf, buf_bytes, stream) -> int:
+    return _call("fa_forward_fp8", q, k, v, signs, o, lse, B, H, N, d, int(causal), float(scale), buf,
+                 buf_bytes, stream)
 
 
 def fa_forward_f32(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
@@ -212,6 +236,59 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
     st = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
                    causal, scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                    _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def _fp8_args(q, k, v, signs):
+    import torch
+
+    _check([q, k, v], ["q", "k", "v"])
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the FP8 path takes bfloat16 tensors")
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != q.shape[-1]
+                              or not signs.is_cuda or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 vector of d entries on the GPU")
+    return q.shape
+
+
+def prepare_fp8(q, k, v, signs=None, buf=None):
+    """Quantise Q, K (rotated by ``signs`` when given) and V to FP8 into a
+    uint8 buffer (layout in include/fa.h) and return it."""
+    import torch
+
+    B, H, N, d = _fp8_args(q, k, v, signs)
+    need = fa_fp8_buffer_size(B, H, N, d)
+    if need == 0:
+        raise FaError(-2)
+    if buf is None:
+        buf = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = fa_fp8_prepare(q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if signs is None else signs.data_ptr(),
+                        B, H, N, d, buf.data_ptr(), buf.numel(), _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return buf
+
+
+def forward_fp8(q, k, v, signs=None, causal: bool = False, scale: float | None = None, buf=None):
+    """FP8 forward with incoherent processing (bf16 in/out, d = 128):
+    returns (o [B,H,N,d], lse [B,H,N])."""
+    import torch
+
+    B, H, N, d = _fp8_args(q, k, v, signs)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_fp8_buffer_size(B, H, N, d)
+    if need == 0:
+        raise FaError(-2)
+    if buf is None:
+        buf = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_forward_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), 0 if signs is None else signs.data_ptr(),
+                        o.data_ptr(), lse.data_ptr(), B, H, N, d, causal, scale, buf.data_ptr(), buf.numel(),
+                        _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return o, lse

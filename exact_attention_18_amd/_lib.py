@@ -27,6 +27,10 @@ SIGNATURES = {
     "fa_forward_block_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_fp8_buffer_size": (_sz, [_i, _i, _i, _i]),
+    "fa_fp8_prepare": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "fa_forward_fp8_prepared": (_i, [_vp, _sz, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "fa_forward_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                          _vp, _sz, _vp]),
     "fa_backward_preprocess": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "f32_path.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "bwd_bf16.hip", "decode_bf16.hip", "fp8_fwd.hip", "f32_path.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -265,6 +265,75 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
                                            static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_fp8_buffer_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d != 128) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL) return 0;
+  return fa::fp8_buffer_layout((long long)bh, N).bytes;
+}
+
+int fa_fp8_prepare(const void* q, const void* k, const void* v, const float* signs, int B, int H, int N, int d,
+                   void* buf, size_t buf_bytes, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, 0, 1.0f, true, &elems);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_fp8_buffer_size(B, H, N, d);
+  if (need == 0 || buf_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * 2;
+  Span ins[4] = {span(q, tb), span(k, tb), span(v, tb), span(signs, 128 * sizeof(float))};
+  const void* inp[4] = {q, k, v, signs};
+  const Span outs[1] = {span(buf, need)};
+  const void* outp[1] = {buf};
+  st = check_buffers(ins, inp, signs != nullptr ? 4 : 3, outs, outp, 1);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_fp8_prepare(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), signs, B * H, N, buf,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int fa_forward_fp8_prepared(const void* buf, size_t buf_bytes, void* o, float* lse, int B, int H, int N, int d,
+                            int causal, float scale, int rotated, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (rotated != 0 && rotated != 1) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_fp8_buffer_size(B, H, N, d);
+  if (need == 0 || buf_bytes < need) return FA_ERR_INVALID_ARG;
+  const Span ins[1] = {span(buf, need)};
+  const void* inp[1] = {buf};
+  const Span outs[2] = {span(o, elems * 2), span(lse, (size_t)B * H * N * sizeof(float))};
+  const void* outp[2] = {o, lse};
+  st = check_buffers(ins, inp, 1, outs, outp, 2);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_fwd_fp8(buf, static_cast<uint16_t*>(o), lse, B * H, N, causal != 0, scale,
+                                       rotated != 0, static_cast<hipStream_t>(stream)));
+}
+
+int fa_forward_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse, int B,
+                   int H, int N, int d, int causal, float scale, void* buf, size_t buf_bytes, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_fp8_buffer_size(B, H, N, d);
+  if (need == 0 || buf_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * 2;
+  Span ins[4] = {span(q, tb), span(k, tb), span(v, tb), span(signs, 128 * sizeof(float))};
+  const void* inp[4] = {q, k, v, signs};
+  const Span outs[3] = {span(o, tb), span(lse, (size_t)B * H * N * sizeof(float)), span(buf, need)};
+  const void* outp[3] = {o, lse, buf};
+  st = check_buffers(ins, inp, signs != nullptr ? 4 : 3, outs, outp, 3);
+  if (st != FA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_fp8_prepare(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                              static_cast<const uint16_t*>(v), signs, B * H, N, buf, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return hip_status(fa::launch_fwd_fp8(buf, static_cast<uint16_t*>(o), lse, B * H, N, causal != 0, scale,
+                                       signs != nullptr, s));
+}
+
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, int d, int causal, float scale, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, stream, false);

@@ -32,6 +32,22 @@ hipError_t launch_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16
                               int BH, int nq, int Nk, int d, bool causal, float scale, void* workspace,
                               hipStream_t stream);
 
+// FP8 forward (d = 128): byte offsets of the sections of the prepared
+// buffer, Np = N rounded up to 64, and its size.
+struct Fp8Buffer {
+  size_t q8, qe, k8, ke, v8, ve, bytes;
+  int Np;
+};
+Fp8Buffer fp8_buffer_layout(long long BH, int N);
+// Quantise Q, K (rotated by diag(signs) * Hadamard when signs != nullptr)
+// and V into `buf`.
+hipError_t launch_fp8_prepare(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* signs, int BH,
+                              int N, void* buf, hipStream_t stream);
+// Attention on a prepared buffer; `rotated` folds the rotation's 1/d into
+// the softmax scale.
+hipError_t launch_fwd_fp8(const void* buf, uint16_t* o, float* lse, int BH, int N, bool causal, float scale,
+                          bool rotated, hipStream_t stream);
+
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,

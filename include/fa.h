@@ -132,6 +132,49 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 
 /*
+ * FP8 forward with incoherent processing (d = 128 only).  The page
+ * "FlashAttention-3 — FlashAttention-3" (section 「3. 量子化誤差を低減した低精度
+ * （FP8）」) multiplies Q and K by a random orthogonal matrix before quantising
+ * them to FP8, which spreads outliers and lowers the FP8 error while leaving
+ * Q K^T unchanged.  Here the matrix is diag(signs) H / sqrt(128) (H the
+ * Sylvester Hadamard matrix); Q, K (rotated) and V are quantised to OCP E4M3,
+ * round to nearest even, with one power-of-two scale per 32 elements (rows of
+ * Q and K; 32 consecutive keys of each column of V), chosen so that nothing
+ * saturates; the attention then runs on the block-scaled FP8 matrix cores,
+ * with P rounded to E4M3 for the P V product and float32 accumulation.
+ * Outputs o (bf16) and lse (float32) mean what they mean for fa_forward.
+ *
+ *   signs : device, 128 floats, each +1 or -1, read only; NULL quantises Q
+ *           and K without rotation (plain FP8, for comparison).
+ *   buf   : device buffer of at least fa_fp8_buffer_size() bytes, 16-byte
+ *           aligned, that receives the quantised operands (layout below).
+ *
+ * fa_forward_fp8 = fa_fp8_prepare then fa_forward_fp8_prepared (rotated =
+ * signs != NULL).  Calling the two halves separately lets a caller reuse the
+ * quantised K and V, or time them apart.
+ *
+ * Layout of buf (sections in this order, each at a 256-byte boundary,
+ * (batch, head) major, Np = N rounded up to 64; rows and keys past N are 0):
+ *   Q8 [B*H][Np][128] E4M3 codes of the (rotated) Q rows;
+ *   QE [B*H][Np][4]   E8M0 scale bytes (127 + t, value 2^t) of their 32-blocks;
+ *   K8, KE            the same for K;
+ *   V8 [B*H][Np/64][128][64]: row c of 64-key tile T holds, for b = 0, 1, the
+ *                     codes of keys 32b .. 32b+31 of column c, key
+ *                     32b + 8j + 4g + i at byte 32b + 16g + 4j + i;
+ *   VE [B*H][Np/64][2][32][4]: VE[T][b][c % 32][c / 32] is the scale byte of
+ *                     keys 32b .. 32b+31 of column c.
+ */
+size_t fa_fp8_buffer_size(int B, int H, int N, int d);
+int fa_fp8_prepare(const void* q, const void* k, const void* v, const float* signs,
+                   int B, int H, int N, int d, void* buf, size_t buf_bytes, void* stream);
+int fa_forward_fp8_prepared(const void* buf, size_t buf_bytes, void* o, float* lse,
+                            int B, int H, int N, int d, int causal, float scale, int rotated,
+                            void* stream);
+int fa_forward_fp8(const void* q, const void* k, const void* v, const float* signs,
+                   void* o, float* lse, int B, int H, int N, int d, int causal, float scale,
+                   void* buf, size_t buf_bytes, void* stream);
+
+/*
  * Backward pass, bf16 in/out, float32 accumulation: the vector-Jacobian
  * product of O with respect to Q, K and V for the incoming gradient dO.
  * The probability matrix is recomputed from q, k and lse rather than stored

@@ -50,6 +50,7 @@ __all__ = [
     "quantize_rows",
     "quantize_v",
     "attention_forward_fp8",
+    "attention_forward_fp8_rows",
 ]
 
 E4M3_MAX = 448.0
@@ -160,9 +161,15 @@ def attention_forward_fp8(q, k, v, signs, causal: bool, scale: float, return_par
     ``q, k, v`` [B, H, N, d] (the exact input values), ``signs`` a length-d
     vector of +-1 (None: no rotation).  Returns (O, LSE) in float64, and with
     ``return_parts`` also a dict with the codes and exponents of Q, K, V,
-    the dequantised operands and ``p_error_bound`` [B, H, N, d] =
-    sum_j p_ij |v'_jc| (the weighted mean of |V'| under the exact P), which
-    bounds how far rounding P to FP8 can move O."""
+    the dequantised operands and ``p_error_bound`` [B, H, N, d].
+
+    The bound: a kernel that rounds each unnormalised weight p_j (largest
+    weight of the row >= 1) to E4M3 changes it by at most 2^-4 max(p_j, 2^-6)
+    (half an ulp of 3 mantissa bits; below the smallest normal 2^-6 the
+    spacing is 2^-9).  In normalised weights P_j that is at most
+    2^-4 max(P_j, 2^-6 max_j P_j), so O_ic moves by at most
+    2^-4 * sum_j max(P_j, 2^-6 max_j P_j) |v'_jc|; ``p_error_bound`` is that
+    sum (without the 2^-4)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -188,8 +195,36 @@ def attention_forward_fp8(q, k, v, signs, causal: bool, scale: float, return_par
             o[b, h] = p @ vd[b, h]
             lse[b, h] = l
             if return_parts:
-                bound[b, h] = p @ np.abs(vd[b, h])
+                w = np.maximum(p, 2.0 ** -6 * p.max(axis=-1, keepdims=True))
+                w = np.where(p > 0, w, 0.0)     # hidden keys carry no weight
+                bound[b, h] = w @ np.abs(vd[b, h])
     if not return_parts:
         return o, lse
     return o, lse, {"q8": q8, "qt": qt, "k8": k8, "kt": kt, "v8": v8, "vt": vt,
                     "qd": qd, "kd": kd, "vd": vd, "p_error_bound": bound}
+
+
+def attention_forward_fp8_rows(q_bh, k_bh, v_bh, rows, signs, causal: bool, scale: float):
+    """``attention_forward_fp8`` for some query rows of one (batch, head):
+    ``q_bh``, ``k_bh``, ``v_bh`` are [N, d]; the rows of Q quantise
+    independently, so only the listed rows are rotated and quantised, while
+    K and V are quantised whole.  Returns (O [len(rows), d], LSE [len(rows)],
+    p_error_bound [len(rows), d])."""
+    rows = np.asarray(rows)
+    q = np.asarray(q_bh, dtype=np.float64)[rows]
+    k = np.asarray(k_bh, dtype=np.float64)
+    v = np.asarray(v_bh, dtype=np.float64)
+    n, d = k.shape
+    if signs is not None:
+        sg = np.asarray(signs, dtype=np.float32)
+        qr, kr = fwht_f32(q.astype(np.float32) * sg), fwht_f32(k.astype(np.float32) * sg)
+        s_scale = float(scale) / d
+    else:
+        qr, kr = q.astype(np.float32), k.astype(np.float32)
+        s_scale = float(scale)
+    qd = _dequant_rows(*quantize_rows(qr))
+    kd = _dequant_rows(*quantize_rows(kr))
+    vd = _dequant_v(*quantize_v(v), n)
+    p, lse = softmax_rows(scores(qd, kd, causal, s_scale, rows=rows))
+    w = np.where(p > 0, np.maximum(p, 2.0 ** -6 * p.max(axis=-1, keepdims=True)), 0.0)
+    return p @ vd, lse, w @ np.abs(vd)

@@ -227,3 +227,51 @@ def test_decode_rejects_overlaps_and_small_workspace(lib):
     p = [ptr(i) for i in range(6)]
     p[3] = p[1] + 256  # o inside k
     assert dec(lib, ptrs=p) == INVALID
+
+
+def test_fp8_buffer_size(lib):
+    # Np = 128 rows for N = 100: 3 code sections of 128 B per row, 3 scale sections of 4 B per row
+    assert lib.fa_fp8_buffer_size(1, 1, 100, 128) == 3 * 128 * 128 + 3 * 128 * 4
+    assert lib.fa_fp8_buffer_size(1, 1, 100, 64) == 0
+    assert lib.fa_fp8_buffer_size(0, 1, 100, 128) == 0
+
+
+def fp8_fwd(lib, B=1, H=1, N=100, d=128, causal=0, scale=0.1, ptrs=None, buf_bytes=None):
+    p = ptrs or [ptr(i) for i in range(7)]   # q k v signs o lse buf
+    if buf_bytes is None:
+        buf_bytes = lib.fa_fp8_buffer_size(B, H, N, 128)
+    return lib.fa_forward_fp8(*p[:6], B, H, N, d, causal, scale, p[6], buf_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(causal=2), dict(scale=-1.0), dict(buf_bytes=100)])
+def test_fp8_rejects_bad_args(lib, kw):
+    assert fp8_fwd(lib, **kw) == INVALID
+
+
+def test_fp8_rejects_d64(lib):
+    assert fp8_fwd(lib, d=64) == UNSUP
+    assert lib.fa_fp8_prepare(*[ptr(i) for i in range(4)], 1, 1, 100, 64, ptr(6), 1 << 20, None) == UNSUP
+    assert lib.fa_forward_fp8_prepared(ptr(6), 1 << 20, ptr(4), ptr(5), 1, 1, 100, 64, 0, 0.1, 1, None) == UNSUP
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 4, 5, 6])
+def test_fp8_rejects_null_and_misaligned(lib, which):
+    p = [ptr(i) for i in range(7)]
+    p[which] = None
+    assert fp8_fwd(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(7)]
+    p[which] = ptr(which, 8)
+    assert fp8_fwd(lib, ptrs=p) == INVALID
+
+
+def test_fp8_rejects_overlaps(lib):
+    p = [ptr(i) for i in range(7)]
+    p[6] = p[4] + 64  # buffer inside o
+    assert fp8_fwd(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(7)]
+    p[6] = p[3]       # buffer on the signs
+    assert fp8_fwd(lib, ptrs=p) == INVALID
+    need = lib.fa_fp8_buffer_size(1, 1, 100, 128)
+    assert lib.fa_forward_fp8_prepared(ptr(6), need, ptr(4), ptr(5), 1, 1, 100, 128, 0, 0.1, 2, None) == INVALID
+    assert lib.fa_forward_fp8_prepared(ptr(6), need - 1, ptr(4), ptr(5), 1, 1, 100, 128, 0, 0.1, 1, None) == INVALID
+    assert lib.fa_forward_fp8_prepared(ptr(6), need, ptr(6) + 32, ptr(5), 1, 1, 100, 128, 0, 0.1, 1, None) == INVALID

@@ -1,0 +1,186 @@
+"""GPU parity of the FP8 forward with incoherent processing.
+
+* The quantised operands the prepare step writes are compared bit for bit
+  with the oracle's codes and exponents (both take every rounding decision in
+  float32 by the same definition).
+* The attention is compared with the oracle's FP8 attention (exact attention
+  on the dequantised operands): LSE within 1e-3; O within the bound that
+  rounding P to E4M3 allows, 2^-4 * p_error_bound (see oracle.fp8), plus the
+  bf16 rounding of O (2^-8 |O|) and 1e-4 for float32 accumulation.
+* Against exact attention of the original inputs, rotation must lower the
+  FP8 error when Q and K carry outliers (the FlashAttention-3 page's claim).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+from oracle import attention_forward, attention_forward_rows
+from oracle import fp8 as ofp8
+from tests.gpu_util import dev, host64, random_inputs
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_18_amd as fa
+
+    fa._lib.load()
+    return fa
+
+
+def _signs_dev(seed):
+    import torch
+
+    return torch.from_numpy(fi.random_signs(seed, D)).to("cuda:0")
+
+
+def _sections(buf, B, H, N):
+    """Split the prepared buffer (uint8 numpy) into its documented sections."""
+    BH, Np = B * H, -(-N // 64) * 64
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    off, out = 0, {}
+    for name, size in (("q8", BH * Np * D), ("qe", BH * Np * 4), ("k8", BH * Np * D), ("ke", BH * Np * 4),
+                       ("v8", BH * Np * D), ("ve", BH * Np * 4)):
+        out[name] = buf[off:off + size]
+        off = up(off + size)
+    out["q8"] = out["q8"].reshape(B, H, Np, D)
+    out["k8"] = out["k8"].reshape(B, H, Np, D)
+    out["qe"] = out["qe"].reshape(B, H, Np, 4)
+    out["ke"] = out["ke"].reshape(B, H, Np, 4)
+    # V8 [T][c][b][g][j][i] holds key 32b + 8j + 4g + i of column c
+    v8 = out["v8"].reshape(B, H, Np // 64, D, 2, 2, 4, 4)
+    out["v8_keys"] = np.transpose(v8, (0, 1, 3, 2, 4, 6, 5, 7)).reshape(B, H, D, Np)
+    ve = out["ve"].reshape(B, H, Np // 64, 2, 32, 4)        # [T][b][c%32][c/32]
+    out["ve_cols"] = np.transpose(ve, (0, 1, 5, 4, 2, 3)).reshape(B, H, D, Np // 32)
+    return out
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300])
+def test_prepare_bit_exact(fa, N, rotate):
+    import torch
+
+    B, H = 2, 2
+    q, k, v = random_inputs(N + 7, (B, H, N, D), "bf16", 3)
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    signs = _signs_dev(N) if rotate else None
+    buf = fa.prepare_fp8(tq, tk, tv, signs)
+    torch.cuda.synchronize()
+    s = _sections(buf.cpu().numpy(), B, H, N)
+    Np = s["q8"].shape[2]
+    sg = fi.random_signs(N, D) if rotate else None
+    for name, x in (("q", q), ("k", k)):
+        xf = fi.bf16_bits_to_f32(x)
+        xr = ofp8.fwht_f32(xf * sg) if rotate else xf
+        codes, t = ofp8.quantize_rows(xr)
+        assert np.array_equal(s[name + "8"][:, :, :N], codes), f"{name} codes"
+        assert np.array_equal(s[name + "e"][:, :, :N].astype(np.int64) - 127, t), f"{name} scales"
+        assert np.all(s[name + "8"][:, :, N:] == 0)
+    codes, t = ofp8.quantize_v(fi.bf16_bits_to_f32(v))
+    assert codes.shape[-1] == Np
+    assert np.array_equal(s["v8_keys"], codes), "V codes"
+    assert np.array_equal(s["ve_cols"].astype(np.int64) - 127, t), "V scales"
+
+
+def _check_attention(fa, B, H, N, causal, rotate, seed):
+    import torch
+
+    q, k, v = random_inputs(seed, (B, H, N, D), "bf16", 3)
+    scale = 1.0 / math.sqrt(D)
+    signs = _signs_dev(seed) if rotate else None
+    o, lse = fa.forward_fp8(dev(q), dev(k), dev(v), signs, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    sg = fi.random_signs(seed, D) if rotate else None
+    ro, rl, parts = ofp8.attention_forward_fp8(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), sg, causal,
+                                               scale, return_parts=True)
+    oh, lh = host64(o), host64(lse)
+    tol = 2.0 ** -4 * parts["p_error_bound"] + 2.0 ** -8 * np.abs(ro) + 1e-4
+    excess = np.abs(oh - ro) - tol
+    assert np.all(np.isfinite(oh)) and excess.max() <= 0, \
+        f"O beyond the P-rounding bound by {excess.max():.3g} (max |dO| {np.abs(oh - ro).max():.3g})"
+    assert np.abs(lh - rl).max() <= 1e-3, f"LSE error {np.abs(lh - rl).max():.3g}"
+    return np.abs(oh - ro).max()
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 128, 129, 300, 1000])
+def test_fp8_forward_vs_oracle(fa, N, causal, rotate):
+    _check_attention(fa, 2, 2, N, causal, rotate, seed=N + 100 * causal)
+
+
+def test_fp8_halves_equal_whole(fa):
+    import torch
+
+    B, H, N = 1, 3, 500
+    q, k, v = (dev(a) for a in random_inputs(12, (B, H, N, D), "bf16", 3))
+    signs = _signs_dev(12)
+    o1, l1 = fa.forward_fp8(q, k, v, signs, causal=True)
+    buf = fa.prepare_fp8(q, k, v, signs)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa.fa_forward_fp8_prepared(buf.data_ptr(), buf.numel(), o2.data_ptr(), l2.data_ptr(), B, H, N, D, 1,
+                                    1 / math.sqrt(D), 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_rotation_lowers_outlier_error(fa):
+    """0.1% of the entries of Q and K multiplied by 10: FP8 error against
+    exact attention (of the bf16 inputs) with and without the rotation."""
+    import torch
+
+    B, H, N = 1, 4, 1024
+    q, k, v = fi.draw_f32(21, (B, H, N, D), 3)
+    q, k = fi.with_outliers(q, 21), fi.with_outliers(k, 22)
+    qb, kb, vb = (fi.f32_to_bf16_bits(a) for a in (q, k, v))
+    tq, tk, tv = dev(qb), dev(kb), dev(vb)
+    ref, _ = attention_forward(fi.exact_f64(qb), fi.exact_f64(kb), fi.exact_f64(vb), False, D ** -0.5)
+    o_plain, _ = fa.forward_fp8(tq, tk, tv, None)
+    o_rot, _ = fa.forward_fp8(tq, tk, tv, _signs_dev(5))
+    torch.cuda.synchronize()
+    e_plain = float(np.sqrt(np.mean((host64(o_plain) - ref) ** 2)))
+    e_rot = float(np.sqrt(np.mean((host64(o_rot) - ref) ** 2)))
+    print(f"FP8 RMSE vs exact: plain {e_plain:.4g}, rotated {e_rot:.4g}, ratio {e_plain / e_rot:.3g}")
+    assert e_rot * 1.25 < e_plain
+
+
+def test_full_size_fp8(fa):
+    """The B=4 H=16 N=4096 d=128 causal workload (inputs x0.5) through the FP8
+    path: sampled rows of sampled heads against the oracle's FP8 attention,
+    and against exact attention for context; repeat launches bit-identical."""
+    import torch
+
+    w = fi.WORKLOADS["bf16_b4h16n4096d128_causal_x0.5"]
+    x = fi.make_inputs(w, with_grad=False)
+    tq, tk, tv = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    signs = _signs_dev(0)
+    o, lse = fa.forward_fp8(tq, tk, tv, signs, causal=True, scale=w.scale)
+    o2, lse2 = fa.forward_fp8(tq, tk, tv, signs, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    rng = np.random.default_rng(4)
+    oh, lh = host64(o), host64(lse)
+    sg = fi.random_signs(0, D)
+    worst_exact = 0.0
+    for (b, h) in sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1], rng.choice(w.N, 40, replace=False)]))
+        qh, kh, vh = (fi.exact_f64(x[n][b, h]) for n in ("q", "k", "v"))
+        ro, rl, bound = ofp8.attention_forward_fp8_rows(qh, kh, vh, rows, sg, True, w.scale)
+        tol = 2.0 ** -4 * bound + 2.0 ** -8 * np.abs(ro) + 1e-4
+        assert np.all(np.abs(oh[b, h, rows] - ro) <= tol)
+        assert np.abs(lh[b, h, rows] - rl).max() <= 1e-3
+        ex, _ = attention_forward_rows(qh, kh, vh, rows, True, w.scale)
+        worst_exact = max(worst_exact, float(np.abs(oh[b, h, rows] - ex).max()))
+    print(f"FP8 max |O - exact| on sampled rows: {worst_exact:.4g}")

@@ -80,3 +80,11 @@ def test_decode_workload_counts():
     x = fi.make_decode_inputs(w)
     assert x["q"].shape == (2, 3, 4, 64) and x["k"].shape == (2, 3, 10, 64) and x["k"].dtype == np.uint16
     assert w.hbm_bytes() == 6 * (2 * 4 * 64 * 2 + 2 * 10 * 64 * 2 + 4 * 4)
+
+
+def test_signs_and_outliers():
+    s = fi.random_signs(3, 128)
+    assert s.dtype == np.float32 and set(np.unique(s)) == {-1.0, 1.0} and np.array_equal(s, fi.random_signs(3, 128))
+    x = np.ones((4, 1000), np.float32)
+    y = fi.with_outliers(x, 1, frac=0.01, factor=10.0)
+    assert set(np.unique(y)) == {1.0, 10.0} and 10 < (y == 10).sum() < 80 and np.all(x == 1)

@@ -199,3 +199,18 @@ def test_fp8_pins_catch_planted_mistake(func, old, new):
     except Exception as e:  # a mutant that breaks a shape or a range also counts as caught
         fails = [repr(e)]
     assert fails != []
+
+
+def test_fp8_rows_equals_full():
+    from oracle import fp8
+    r = np.random.default_rng(9)
+    q, k, v = (r.standard_normal((1, 1, 150, 128)) for _ in range(3))
+    sg = np.where(r.random(128) < 0.5, -1.0, 1.0)
+    rows = np.array([0, 5, 63, 64, 149])
+    for signs in (None, sg):
+        for causal in (False, True):
+            o, l, parts = fp8.attention_forward_fp8(q, k, v, signs, causal, 0.09, return_parts=True)
+            orow, lrow, brow = fp8.attention_forward_fp8_rows(q[0, 0], k[0, 0], v[0, 0], rows, signs, causal, 0.09)
+            assert np.allclose(orow, o[0, 0, rows], rtol=0, atol=1e-13)
+            assert np.allclose(lrow, l[0, 0, rows], rtol=0, atol=1e-13)
+            assert np.allclose(brow, parts["p_error_bound"][0, 0, rows], rtol=0, atol=1e-13)
