@@ -40,6 +40,8 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, 8 TB/s
 PEAK_FP8_TFLOPS = 5033.2   # dense FP8 matrix cores, twice the bf16 rate
 DEFAULT_WORKLOAD = "bf16_b8h16n2048d128_causal_fwdbwd"
+CLOCK_WARMUP_S = 1.0   # untimed work before the timed steps (clock ramp-up)
+CLOCK_REWARM_S = 0.3   # untimed burst before each secondary measurement
 HEADLINE_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal"]
 
 
@@ -195,6 +197,15 @@ def main():
         ]
     step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
 
+    def clock_warm(fn, seconds=CLOCK_WARMUP_S):
+        """Run ``fn`` untimed, back to back, for about ``seconds``."""
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+
     def run_step(evs=None):
         for i, (name, fn, _) in enumerate(kernels):
             if evs is not None:
@@ -205,6 +216,9 @@ def main():
             if evs is not None:
                 evs[i][1].record(stream)
 
+    # The GPU runs at lower clocks for roughly its first second of work, so
+    # the step runs untimed for CLOCK_WARMUP_S before the W warm-up steps.
+    clock_warm(run_step)
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -230,7 +244,9 @@ def main():
                     for n, _, f in kernels}
 
     def time_launches(fn, n=10, warm=3):
-        """Mean HIP-event time (ms) of ``fn`` launched ``n`` times on ``stream``."""
+        """Mean HIP-event time (ms) of ``fn`` launched ``n`` times on ``stream``,
+        after a short untimed burst that brings the clocks back up."""
+        clock_warm(fn, CLOCK_REWARM_S)
         for _ in range(warm):
             fn()
         evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -355,6 +371,7 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": bool(causal),
                    "step": "forward+backward" if w.backward else "forward",
                    "step_gflop": round(step_flops / 1e9, 2), "parallelism": "single GPU",
+                   "clock_warmup_s": CLOCK_WARMUP_S,
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
