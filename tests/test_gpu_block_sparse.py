@@ -157,3 +157,34 @@ def test_full_size_block_sparse(fa, name):
             mask, BLK, w.causal, w.scale)
         assert max_abs(oh[b, h, rows], ro) <= TOL_O
         assert max_abs(lh[b, h, rows], rl) <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_scale_zero_is_mean_of_visible(fa, causal):
+    """scale = 0: uniform weights over the visible keys, so O is the mean of
+    the visible V rows and LSE = log(count) (closed form, no oracle call)."""
+    import torch
+
+    N, nb = 300, 3
+    mask = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 0]], np.uint8)
+    q, k, v = random_inputs(31, (1, 2, N, 64), "bf16", 3)
+    o, lse = fa.forward_block_sparse(dev(q), dev(k), dev(v), _mask_dev(mask), causal=causal, scale=0.0)
+    torch.cuda.synchronize()
+    vis = oracle.block_visibility(mask, N, BLK)
+    if causal:
+        vis &= np.tril(np.ones((N, N), bool))
+    vf = fi.exact_f64(v)
+    cnt = vis.sum(1)
+    mean = (vis[None, None] @ vf) / np.maximum(cnt, 1)[None, None, :, None]
+    oh, lh = host64(o), host64(lse)
+    live = cnt > 0
+    assert max_abs(oh[:, :, live], mean[:, :, live]) <= TOL_O
+    assert np.abs(lh[:, :, live] - np.log(cnt[live])).max() <= TOL_LSE
+    assert np.all(oh[:, :, ~live] == 0) and np.all(np.isneginf(lh[:, :, ~live]))
+
+
+def test_block_sparse_mid_size_d64(fa):
+    N = 2048
+    nb = N // BLK
+    mask = fi.local_global_block_mask(nb, 1, 1)
+    _check(fa, 1, 4, N, 64, True, mask, seed=8)

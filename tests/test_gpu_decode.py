@@ -110,3 +110,32 @@ def test_full_size_decode(fa, name):
     ro, rl = oracle.attention_forward_kv(fi.exact_f64(x["q"]), fi.exact_f64(x["k"]), fi.exact_f64(x["v"]),
                                          w.causal, w.scale)
     _compare(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("Nq", [1, 6])
+def test_decode_scale_zero_is_mean(fa, Nq):
+    """scale = 0: each query's output is the mean of the values it sees and
+    LSE = log(count) (closed form)."""
+    import torch
+
+    B, H, Nk, d = 1, 2, 777, 128
+    w = fi.DecodeWorkload("t", B, H, Nq, Nk, d, True, 5)
+    x = fi.make_decode_inputs(w)
+    o, lse = fa.decode(dev(x["q"]), dev(x["k"]), dev(x["v"]), causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    vf = fi.exact_f64(x["v"])
+    for i in range(Nq):
+        cnt = Nk - Nq + i + 1
+        assert max_abs(host64(o)[:, :, i], vf[:, :, :cnt].mean(axis=2)) <= TOL_O
+        assert np.abs(host64(lse)[:, :, i] - np.log(cnt)).max() <= TOL_LSE
+
+
+def test_decode_rejects_bad_tensors(fa):
+    import torch
+
+    q = torch.zeros((1, 2, 9, 128), dtype=torch.bfloat16, device="cuda:0")   # Nq = 9 > 8
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(fa.FaError):
+        fa.decode(q, k, k)
+    with pytest.raises(ValueError):
+        fa.decode(q[:, :, :4], k, k)          # not contiguous

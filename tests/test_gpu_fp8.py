@@ -184,3 +184,31 @@ def test_full_size_fp8(fa):
         ex, _ = attention_forward_rows(qh, kh, vh, rows, True, w.scale)
         worst_exact = max(worst_exact, float(np.abs(oh[b, h, rows] - ex).max()))
     print(f"FP8 max |O - exact| on sampled rows: {worst_exact:.4g}")
+
+
+def test_fp8_scale_zero_is_mean(fa):
+    """scale = 0: uniform weights, so O is the mean of the visible rows of the
+    dequantised V (to within P's rounding, exact here: p = 1 is an E4M3 value)."""
+    import torch
+
+    B, H, N = 1, 2, 200
+    q, k, v = random_inputs(41, (B, H, N, D), "bf16", 3)
+    o, lse = fa.forward_fp8(dev(q), dev(k), dev(v), _signs_dev(3), causal=True, scale=0.0)
+    torch.cuda.synchronize()
+    _, _, parts = ofp8.attention_forward_fp8(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), None, True, 0.0,
+                                             return_parts=True)
+    vd = parts["vd"]
+    mean = np.cumsum(vd, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.abs(host64(o) - mean).max() <= 2.0 ** -8 * np.abs(mean).max() + 1e-4
+    assert np.abs(host64(lse) - np.log(np.arange(1, N + 1))).max() <= 1e-3
+
+
+def test_fp8_rejects_bad_inputs(fa):
+    import torch
+
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(fa.FaError):
+        fa.forward_fp8(q, q, q)                       # d = 64 is not supported
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError):
+        fa.forward_fp8(q, q, q, torch.ones(64, device="cuda:0"))   # signs of the wrong length
