@@ -22,6 +22,7 @@ __all__ = [
     "FaError",
     "fa_forward",
     "fa_forward_block_sparse",
+    "fa_block_sparse_workspace_size",
     "fa_decode",
     "fa_fp8_buffer_size",
     "fa_fp8_prepare",
@@ -67,9 +68,13 @@ def fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
     return _call("fa_forward", q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream)
 
 
-def fa_forward_block_sparse(q, k, v, o, lse, block_mask, B, H, N, d, causal, scale, stream) -> int:
+def fa_forward_block_sparse(q, k, v, o, lse, block_mask, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
     return _call("fa_forward_block_sparse", q, k, v, o, lse, block_mask, B, H, N, d, int(causal),
-                 float(scale), stream)
+                 float(scale), ws, ws_bytes, stream)
+
+
+def fa_block_sparse_workspace_size(B, H, N, d) -> int:
+    return int(_call("fa_block_sparse_workspace_size", B, H, N, d))
 
 
 def fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ws, ws_bytes, stream) -> int:
@@ -182,12 +187,15 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None):
     return o, lse
 
 
-def forward_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None):
+def forward_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None,
+                         balance: bool = True, workspace=None):
     """Block-sparse attention (bf16): query i sees key j iff
     ``block_mask[i // 128, j // 128]`` is nonzero (and j <= i when causal).
 
     ``block_mask`` is a [ceil(N/128), ceil(N/128)] uint8 or bool tensor on the
-    same GPU.  Rows that see no key get o = 0 and lse = -inf.
+    same GPU.  Rows that see no key get o = 0 and lse = -inf.  With
+    ``balance`` heavy mask rows are split over several workgroups (a
+    workspace is allocated unless one is passed).
     """
     import torch
 
@@ -204,8 +212,15 @@ def forward_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if balance:
+        need = fa_block_sparse_workspace_size(B, H, N, d)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = fa_forward_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                 block_mask.data_ptr(), B, H, N, d, causal, scale, _stream(q.device))
+                                 block_mask.data_ptr(), B, H, N, d, causal, scale, ws_ptr, ws_bytes,
+                                 _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return o, lse

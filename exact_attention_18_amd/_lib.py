@@ -24,7 +24,8 @@ _sz = ctypes.c_size_t
 # name -> (restype, argtypes), in the order of include/fa.h
 SIGNATURES = {
     "fa_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
-    "fa_forward_block_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
+    "fa_forward_block_sparse": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_block_sparse_workspace_size": (_sz, [_i, _i, _i, _i]),
     "fa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "fa_fp8_buffer_size": (_sz, [_i, _i, _i, _i]),

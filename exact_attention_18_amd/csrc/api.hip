@@ -209,26 +209,37 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                       causal, scale, stream, true);
 }
 
+size_t fa_block_sparse_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  if (N > 4096 * FA_BLOCK_SPARSE_BLOCK) return 0;   // the row plan is built in one workgroup's LDS
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  if (bh > 0x7fffffffULL) return 0;
+  return fa::sparse_workspace_layout((long long)bh, N, d).bytes;
+}
+
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                             const unsigned char* block_mask, int B, int H, int N, int d, int causal,
-                            float scale, void* stream) {
+                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
   size_t elems = 0;
   int st = check_common(B, H, N, d, causal, scale, true, &elems);
   if (st != FA_OK) return st;
   if (block_mask == nullptr) return FA_ERR_INVALID_ARG;
   const size_t nb = ((size_t)N + FA_BLOCK_SPARSE_BLOCK - 1) / FA_BLOCK_SPARSE_BLOCK;
   const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
+  const size_t need = workspace != nullptr ? fa_block_sparse_workspace_size(B, H, N, d) : 0;
+  if (workspace != nullptr && (need == 0 || workspace_bytes < need)) return FA_ERR_INVALID_ARG;
   const Span ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
   const void* inp[3] = {q, k, v};
-  const Span outs[2] = {span(o, tb), span(lse, lb)};
-  const void* outp[2] = {o, lse};
-  st = check_buffers(ins, inp, 3, outs, outp, 2);
+  const Span outs[3] = {span(o, tb), span(lse, lb), span(workspace, need)};
+  const void* outp[3] = {o, lse, workspace};
+  st = check_buffers(ins, inp, 3, outs, outp, workspace != nullptr ? 3 : 2);
   if (st != FA_OK) return st;
   const Span ms = span(block_mask, nb * nb);
-  if (overlap(ms, outs[0]) || overlap(ms, outs[1])) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < (workspace != nullptr ? 3 : 2); ++i)
+    if (overlap(ms, outs[i])) return FA_ERR_INVALID_ARG;
   return hip_status(fa::launch_fwd_bf16_block_sparse(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<uint16_t*>(o), lse, block_mask, B * H, N, d, causal != 0, scale,
+      static_cast<uint16_t*>(o), lse, block_mask, B * H, N, d, causal != 0, scale, workspace,
       static_cast<hipStream_t>(stream)));
 }
 

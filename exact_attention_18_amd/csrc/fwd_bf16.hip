@@ -344,6 +344,317 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Balanced block-sparse forward.  A block mask can give some query blocks
+// far more visible key blocks than others (a "global" query row sees them
+// all); one workgroup per query block then leaves the whole launch waiting
+// for the heaviest row.  A plan kernel counts every mask row and splits the
+// rows holding more than twice the mean into parts of about the mean; a
+// persistent kernel walks the list of (row, part) items; the parts of split
+// rows leave partial results (unnormalised O, reference max, row sum) that a
+// merge kernel combines exactly as the online softmax combines tiles.  Rows
+// that are not split follow the same tile sequence as the one-pass kernel
+// and give bit-identical results.
+//
+// plan (int32): [0] items per head P, [1] partial slots per head, [2] mean,
+// then row_cnt[nqb], row_parts[nqb], row_first[nqb], row_slot[nqb],
+// item_qb[3 nqb], item_part[3 nqb].  With split iff cnt > 2 mean and
+// parts = min(16, ceil(cnt / mean)): fewer than nqb / 2 rows split, so P < 2.5 nqb and
+// the split rows use fewer than 1.5 nqb slots (2 nqb are allocated).
+
+constexpr int SPARSE_MAX_PARTS = 16;   // parts per split row (bounds the merge's unrolled loads)
+constexpr int SPARSE_PLAN_MAX_NQB = 4096;  // plan kept in LDS: 3 ints per query block
+
+__global__ void __launch_bounds__(256)
+sparse_plan_kernel(const uint8_t* __restrict__ bmask, int nqb, int causal, int* __restrict__ plan,
+                   int* __restrict__ counters, int n_counters) {
+  for (int i = threadIdx.x; i < n_counters; i += 256) counters[i] = 0;
+  __shared__ int s_cnt[SPARSE_PLAN_MAX_NQB], s_parts[SPARSE_PLAN_MAX_NQB], s_first[SPARSE_PLAN_MAX_NQB];
+  int* cnt = plan + 4;
+  int* parts = cnt + nqb;
+  int* first = parts + nqb;
+  int* slot = first + nqb;
+  int* item_qb = slot + nqb;
+  int* item_part = item_qb + 3 * nqb;
+  for (int qb = threadIdx.x; qb < nqb; qb += 256) s_cnt[qb] = 0;
+  __syncthreads();
+  // Count the visible blocks of every row: the mask is read as a flat array,
+  // 16 entries per thread per pass, with the loads of a pass issued together.
+  const int cells = nqb * nqb;   // nqb <= 4096, so this fits in 32 bits
+  for (int c0 = 16 * threadIdx.x; c0 < cells; c0 += 16 * 256) {
+    uint8_t v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = c0 + i < cells ? bmask[c0 + i] : 0;
+    int qb = c0 / nqb, kb = c0 - qb * nqb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (v[i] != 0 && (!causal || kb <= qb)) atomicAdd(&s_cnt[qb], 1);
+      if (++kb == nqb) {
+        kb = 0;
+        ++qb;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long total = 0;
+    for (int qb = 0; qb < nqb; ++qb) total += s_cnt[qb];
+    const int mean = (int)max(1LL, (total + nqb - 1) / nqb);
+    int P = 0, S = 0;
+    for (int qb = 0; qb < nqb; ++qb) {
+      const int c = s_cnt[qb];
+      const int p = c > 2 * mean ? min(SPARSE_MAX_PARTS, (c + mean - 1) / mean) : 1;
+      s_parts[qb] = p;
+      s_first[qb] = P;
+      slot[qb] = p > 1 ? S : -1;
+      P += p;
+      if (p > 1) S += p;
+    }
+    plan[0] = P;
+    plan[1] = S;
+    plan[2] = mean;
+  }
+  __syncthreads();
+  for (int qb = threadIdx.x; qb < nqb; qb += 256) {
+    cnt[qb] = s_cnt[qb];
+    parts[qb] = s_parts[qb];
+    first[qb] = s_first[qb];
+    for (int p = 0; p < s_parts[qb]; ++p) {
+      item_qb[s_first[qb] + p] = qb;
+      item_part[s_first[qb] + p] = p;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FA_FWD_WAVES_PER_SIMD, FA_FWD_WAVES_PER_SIMD)))
+fwd_sparse_balanced_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+                           int N, int nqb, int BH, float c, const uint8_t* __restrict__ bmask,
+                           const int* __restrict__ plan, float* __restrict__ part_o,
+                           float* __restrict__ part_ml, int* __restrict__ counters) {
+  using L = Lds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  __shared__ long long s_item;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int P = plan[0];
+  const int* row_cnt = plan + 4;
+  const int* row_parts = row_cnt + nqb;
+  const int* row_slot = row_parts + 2 * nqb;
+  const int* item_qb = row_slot + nqb;
+  const int* item_part = item_qb + 3 * nqb;
+  const int slots = 2 * nqb;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const long long items = (long long)BH * P;
+
+  // Items are split into 8 contiguous ranges, one per XCD (the dispatcher
+  // hands workgroup ids to the XCDs round-robin), so the items of a head
+  // share one XCD's L2 as in the one-pass grid; within its range a
+  // workgroup takes the next item from that XCD's counter (zeroed by the
+  // plan kernel), so the load evens out to within one item.  A grid of fewer
+  // than 8 workgroups uses one counter over all items.
+  const int x = gridDim.x >= 8 ? (int)(blockIdx.x & 7) : 0;
+  const long long it0 = gridDim.x >= 8 ? x * items / 8 : 0;
+  const long long it1 = gridDim.x >= 8 ? (x + 1) * items / 8 : items;
+  while (true) {
+    if (tid == 0) s_item = it0 + atomicAdd(&counters[x], 1);
+    __syncthreads();
+    const long long it = s_item;
+    if (it >= it1) break;   // uniform: every wave read the same value
+    const int bh = (int)(it / P), i = (int)(it - (long long)bh * P);
+    const int qb = item_qb[i], part = item_part[i], parts = row_parts[qb], cnt = row_cnt[qb];
+    // this item's visible blocks: ordinals [o0, o1) among the row's visible blocks
+    const int o0 = (int)((long long)part * cnt / parts), o1 = (int)((long long)(part + 1) * cnt / parts);
+    const size_t base = (size_t)bh * N * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+    const int q0 = qb * BR, qw = q0 + wave * 32, myq = qw + l32;
+    bf16x8 qf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[ks] = bf16x8_from(buf_load16(qrs, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2)));
+    const int kend = CAUSAL ? qb + 1 : nqb;            // key blocks that can be visible
+    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_end + BC - 1) / BC;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    // Visible-block walk over the mask row (64 entries per ballot).
+    const uint8_t* mrow = bmask + (size_t)qb * nqb;
+    int win = -1;
+    uint64_t bits = 0;
+    auto window = [&](int w) {
+      if (w != win) {
+        win = w;
+        const int e = 64 * w + lane;
+        bits = __ballot(e < kend && mrow[e] != 0);
+      }
+      return bits;
+    };
+    auto next_visible = [&](int b) {  // smallest visible block >= b, or kend
+      while (b < kend) {
+        const uint64_t rest = window(b >> 6) >> (b & 63);
+        if (rest) return b + (int)__builtin_ctzll(rest);
+        b = 64 * ((b >> 6) + 1);
+      }
+      return kend;
+    };
+    auto nth_visible = [&](int o) {  // the o-th visible block (from 0), or kend
+      for (int w = 0; 64 * w < kend; ++w) {
+        uint64_t b = window(w);
+        const int n = __builtin_popcountll(b);
+        if (o < n) {
+          for (int t = 0; t < o; ++t) b &= b - 1;
+          return 64 * w + (int)__builtin_ctzll(b);
+        }
+        o -= n;
+      }
+      return kend;
+    };
+    int blk = o1 > o0 ? nth_visible(o0) : kend;
+    int blocks_left = o1 - o0;                        // blocks of this item not yet finished
+    int j = blk < kend ? 2 * blk : ntiles;
+    TileRegs<D> regs;
+    if (j < ntiles) {
+      load_tile<D>(regs, krs, vrs, j * BC, tid);
+      store_tile<D>(regs, smem, tid);
+    }
+    __syncthreads();
+    int slot = 0;
+    while (j < ntiles) {
+      int jn;
+      if ((j & 1) == 0 && j + 1 < ntiles) {
+        jn = j + 1;
+      } else {
+        --blocks_left;
+        jn = blocks_left > 0 ? 2 * next_visible((j >> 1) + 1) : ntiles;
+        if (jn > ntiles) jn = ntiles;
+      }
+      const uint16_t* Ks = smem + slot * L::STAGE;
+      const uint16_t* Vs = Ks + L::K_ELEMS;
+      const int kv0 = j * BC;
+      if (jn < ntiles) load_tile<D>(regs, krs, vrs, jn * BC, tid);
+      if (!CAUSAL || kv0 <= qw + 31) {
+        const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
+        tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
+      }
+      if (jn < ntiles) store_tile<D>(regs, smem + (slot ^ 1) * L::STAGE, tid);
+      __syncthreads();
+      slot ^= 1;
+      j = jn;
+    }
+
+    const float ltot = sum_halves(lsum);
+    if (myq < N) {
+      if (parts == 1) {
+        const float inv = ltot > 0.f ? rcp_hw(ltot) : 0.f;
+        uint16_t* orow = O + base + (size_t)myq * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            u32x2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
+                       pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
+          }
+        if (g == 0) LSE[(size_t)bh * N + myq] = ltot > 0.f ? (m + log2_hw(ltot)) * kLn2 : -INFINITY;
+      } else {
+        const size_t prow = ((size_t)bh * slots + row_slot[qb] + part) * BR + (myq - q0);
+        float* po = part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            *reinterpret_cast<f32x4*>(po + db * 32 + 8 * a + 4 * g) =
+                f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]};
+        if (g == 0) *reinterpret_cast<f32x2*>(part_ml + prow * 2) = f32x2{m, ltot};
+      }
+    }
+  }
+}
+
+// Combine the parts of split rows: four workgroups per (batch*head, query
+// block), 32 rows each; rows that were not split return at once.  Each
+// thread merges 4 columns of one row, with the loads of all parts issued
+// together.
+template <int D>
+__global__ void __launch_bounds__(256)
+sparse_merge_kernel(const int* __restrict__ plan, const float* __restrict__ part_o,
+                    const float* __restrict__ part_ml, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
+                    int nqb) {
+  const int blk = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int bh = blk / nqb, qb = blk - bh * nqb;
+  const int* row_parts = plan + 4 + nqb;
+  const int* row_slot = row_parts + 2 * nqb;
+  const int parts = row_parts[qb];
+  if (parts == 1) return;
+  const size_t s0 = (size_t)bh * 2 * nqb + row_slot[qb];
+  constexpr int C4 = D / 4;
+  for (int idx = threadIdx.x; idx < 32 * C4; idx += 256) {
+    const int r = quarter * 32 + idx / C4, c4 = 4 * (idx % C4);
+    const int q = qb * BR + r;
+    if (q >= N) break;
+    f32x2 ml[SPARSE_MAX_PARTS];
+    f32x4 ov[SPARSE_MAX_PARTS];
+#pragma unroll
+    for (int p = 0; p < SPARSE_MAX_PARTS; ++p)
+      if (p < parts) {
+        const size_t pr = (s0 + p) * BR + r;
+        ml[p] = *reinterpret_cast<const f32x2*>(part_ml + pr * 2);
+        ov[p] = *reinterpret_cast<const f32x4*>(part_o + pr * D + c4);
+      }
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < SPARSE_MAX_PARTS; ++p)
+      if (p < parts) M = max_nan(M, ml[p][0]);
+    float Lsum = 0.f;
+    f32x4 acc = {};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int p = 0; p < SPARSE_MAX_PARTS; ++p)
+        if (p < parts) {
+          const float f = exp2_hw(ml[p][0] - M);   // 0 for a part with no visible key
+          Lsum += ml[p][1] * f;
+          acc += ov[p] * f;
+        }
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(O + ((size_t)bh * N + q) * D + c4) = w;
+    if (c4 == 0) LSE[(size_t)bh * N + q] = Lsum > 0.f ? (M + log2_hw(Lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_sparse_balanced(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                                  const uint8_t* bmask, int BH, int N, float scale, void* workspace,
+                                  hipStream_t stream) {
+  const int nqb = (N + BR - 1) / BR;
+  if ((long long)N * D * 2 >= (1LL << 31) || nqb > SPARSE_PLAN_MAX_NQB || (long long)BH * nqb * 4 > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  const SparseWorkspace w = sparse_workspace_layout(BH, N, D);
+  char* ws = static_cast<char*>(workspace);
+  int* plan = reinterpret_cast<int*>(ws);
+  float* po = reinterpret_cast<float*>(ws + w.part_o);
+  float* pml = reinterpret_cast<float*>(ws + w.part_ml);
+  int* counters = reinterpret_cast<int*>(ws + w.counters);
+  hipLaunchKernelGGL(sparse_plan_kernel, dim3(1), dim3(256), 0, stream, bmask, nqb, CAUSAL ? 1 : 0, plan, counters,
+                     8);
+  long long wgs = min((long long)BH * nqb, 512LL);
+  if (wgs >= 8) wgs &= ~7LL;   // a multiple of 8: the same number of workgroups per XCD
+  hipLaunchKernelGGL((fwd_sparse_balanced_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(NT), 0, stream, q, k, v, o,
+                     lse, N, nqb, BH, score_coef(scale), bmask, plan, po, pml, counters);
+  hipLaunchKernelGGL((sparse_merge_kernel<D>), dim3((unsigned)((long long)BH * nqb * 4)), dim3(256), 0, stream, plan,
+                     po, pml, o, lse, N, nqb);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
@@ -356,9 +667,31 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
   return hipErrorInvalidValue;
 }
 
+SparseWorkspace sparse_workspace_layout(long long BH, int N, int d) {
+  SparseWorkspace w;
+  const long long nqb = (N + BR - 1) / BR;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.plan = 0;
+  w.counters = up((size_t)(4 + 4 * nqb + 6 * nqb) * sizeof(int));
+  w.part_o = up(w.counters + 8 * sizeof(int));
+  w.part_ml = up(w.part_o + (size_t)BH * 2 * nqb * BR * d * sizeof(float));
+  w.bytes = up(w.part_ml + (size_t)BH * 2 * nqb * BR * 2 * sizeof(float));
+  return w;
+}
+
 hipError_t launch_fwd_bf16_block_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         uint16_t* o, float* lse, const uint8_t* block_mask, int BH,
-                                        int N, int d, bool causal, float scale, hipStream_t stream) {
+                                        int N, int d, bool causal, float scale, void* workspace,
+                                        hipStream_t stream) {
+  if (workspace != nullptr) {
+    if (d == 64)
+      return causal ? launch_sparse_balanced<64, true>(q, k, v, o, lse, block_mask, BH, N, scale, workspace, stream)
+                    : launch_sparse_balanced<64, false>(q, k, v, o, lse, block_mask, BH, N, scale, workspace, stream);
+    if (d == 128)
+      return causal ? launch_sparse_balanced<128, true>(q, k, v, o, lse, block_mask, BH, N, scale, workspace, stream)
+                    : launch_sparse_balanced<128, false>(q, k, v, o, lse, block_mask, BH, N, scale, workspace, stream);
+    return hipErrorInvalidValue;
+  }
   if (d == 64)
     return causal ? launch<64, true, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask)
                   : launch<64, false, true>(q, k, v, o, lse, BH, N, scale, stream, block_mask);

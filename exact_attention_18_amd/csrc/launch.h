@@ -14,9 +14,17 @@ hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            hipStream_t stream);
 
 // Block-sparse forward: block_mask is [ceil(N/128)][ceil(N/128)] bytes.
+// With a workspace (laid out by sparse_workspace_layout) heavy mask rows are
+// split over several workgroups and merged; without one, one workgroup per
+// query block.
+struct SparseWorkspace {
+  size_t plan, counters, part_o, part_ml, bytes;
+};
+SparseWorkspace sparse_workspace_layout(long long BH, int N, int d);
 hipError_t launch_fwd_bf16_block_sparse(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                         uint16_t* o, float* lse, const uint8_t* block_mask, int BH,
-                                        int N, int d, bool causal, float scale, hipStream_t stream);
+                                        int N, int d, bool causal, float scale, void* workspace,
+                                        hipStream_t stream);
 
 // Decode (1 <= nq <= 8 queries over Nk keys), split over key chunks.  The
 // workspace layout and size follow decode_split(); both the launcher and the

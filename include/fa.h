@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 enum fa_status {
   FA_OK = 0,
@@ -91,12 +91,30 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
  *   block_mask      : device, nb x nb bytes row-major (query block major),
  *                     nonzero = visible, read only, any alignment; one mask
  *                     shared by every (batch, head).
- * A query row that sees no key gets o = 0 and lse = -inf.  With every block
- * visible the result equals fa_forward's (same arithmetic, tile by tile).
+ *   workspace       : NULL, or device scratch of at least
+ *                     fa_block_sparse_workspace_size() bytes, 16-byte
+ *                     aligned (contents on entry ignored, on return
+ *                     unspecified).  NULL: one workgroup per query block.
+ *                     With a workspace the rows of the mask are counted on
+ *                     the device first; rows with more than twice the mean
+ *                     count of visible blocks are split over several
+ *                     workgroups and their partial results merged, which
+ *                     keeps a few dense rows (e.g. global tokens) from
+ *                     setting the running time.  Rows that are not split
+ *                     give the same bits either way.
+ * A query row that sees no key gets o = 0 and lse = -inf.  Without a
+ * workspace and with every block visible the result equals fa_forward's
+ * (same arithmetic, tile by tile).
  */
 int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                             const unsigned char* block_mask, int B, int H, int N, int d,
-                            int causal, float scale, void* stream);
+                            int causal, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Bytes of workspace fa_forward_block_sparse uses to split heavy rows (0 if
+ * a size is out of range; N above 4096 * 128 = 524288 takes no workspace).
+ * Pure host function. */
+size_t fa_block_sparse_workspace_size(int B, int H, int N, int d);
 
 /* Largest number of new queries per (batch, head) fa_decode accepts. */
 #define FA_DECODE_MAX_QUERIES 8

@@ -144,9 +144,9 @@ def test_python_binding_names_match_abi():
     assert fa.fa_status_string(-1).startswith("FA_ERR_INVALID_ARG")
 
 
-def sparse(lib, B=1, H=1, N=300, d=64, causal=0, scale=0.125, ptrs=None):
+def sparse(lib, B=1, H=1, N=300, d=64, causal=0, scale=0.125, ptrs=None, ws=None, ws_bytes=0):
     p = ptrs or [ptr(i) for i in range(6)]
-    return lib.fa_forward_block_sparse(*p, B, H, N, d, causal, scale, None)
+    return lib.fa_forward_block_sparse(*p, B, H, N, d, causal, scale, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(causal=3), dict(scale=-1.0),
@@ -275,3 +275,11 @@ def test_fp8_rejects_overlaps(lib):
     assert lib.fa_forward_fp8_prepared(ptr(6), need, ptr(4), ptr(5), 1, 1, 100, 128, 0, 0.1, 2, None) == INVALID
     assert lib.fa_forward_fp8_prepared(ptr(6), need - 1, ptr(4), ptr(5), 1, 1, 100, 128, 0, 0.1, 1, None) == INVALID
     assert lib.fa_forward_fp8_prepared(ptr(6), need, ptr(6) + 32, ptr(5), 1, 1, 100, 128, 0, 0.1, 1, None) == INVALID
+
+
+def test_block_sparse_workspace(lib):
+    need = lib.fa_block_sparse_workspace_size(1, 1, 300, 64)
+    assert need > 0 and lib.fa_block_sparse_workspace_size(1, 1, 300, 96) == 0
+    assert sparse(lib, ws=ptr(7), ws_bytes=need - 1) == INVALID         # too small
+    assert sparse(lib, ws=ptr(7, 8), ws_bytes=need) == INVALID          # misaligned
+    assert sparse(lib, ws=ptr(3, 16), ws_bytes=need) == INVALID         # inside o

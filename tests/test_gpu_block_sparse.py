@@ -104,11 +104,13 @@ def test_all_visible_equals_dense_bitwise(fa, d, causal):
     N = 777
     nb = -(-N // BLK)
     q, k, v = (dev(a) for a in random_inputs(4, (2, 3, N, d), "bf16", 3))
-    o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.ones((nb, nb), np.uint8)), causal=causal)
     od, ld = fa.forward(q, k, v, causal=causal)
-    torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), od.view(torch.int16))
-    assert torch.equal(lse, ld)
+    for balance in (False, True):   # every row has the same count: nothing is split either way
+        o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.ones((nb, nb), np.uint8)), causal=causal,
+                                         balance=balance)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), od.view(torch.int16))
+        assert torch.equal(lse, ld)
 
 
 def test_block_diagonal_equals_independent_segments(fa):
@@ -188,3 +190,64 @@ def test_block_sparse_mid_size_d64(fa):
     nb = N // BLK
     mask = fi.local_global_block_mask(nb, 1, 1)
     _check(fa, 1, 4, N, 64, True, mask, seed=8)
+
+
+def _heavy_mask(nb, seed):
+    """A sparse random mask plus one dense query-block row (a "global" row):
+    the kind of mask whose rows the balanced path splits."""
+    m = fi.random_block_mask(seed, nb, 0.15)
+    np.fill_diagonal(m, 1)
+    m[nb // 3, :] = 1
+    m[nb - 1, :] = 1   # dense also under a causal mask
+    return m
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1500, 2048])
+def test_balanced_split_rows_vs_oracle(fa, N, d, causal):
+    nb = -(-N // BLK)
+    mask = _heavy_mask(nb, N + d)
+    if not causal:
+        mask[0, :] = 1   # a second dense row
+    _check(fa, 1, 3, N, d, causal, mask, seed=N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_balanced_unsplit_rows_bitwise_equal_one_pass(fa, causal):
+    """Rows the plan does not split follow the one-pass tile sequence: same
+    bits.  The dense row is split; its result stays within tolerance of the
+    oracle (checked above)."""
+    import torch
+
+    N = 2048
+    nb = N // BLK
+    mask = _heavy_mask(nb, 5)
+    q, k, v = (dev(a) for a in random_inputs(17, (1, 2, N, 128), "bf16", 3))
+    tm = _mask_dev(mask)
+    o1, l1 = fa.forward_block_sparse(q, k, v, tm, causal=causal, balance=False)
+    o2, l2 = fa.forward_block_sparse(q, k, v, tm, causal=causal, balance=True)
+    torch.cuda.synchronize()
+    cnt = mask.sum(1) if not causal else np.tril(mask).sum(1)
+    mean = max(1, -(-int(cnt.sum()) // nb))
+    unsplit = np.repeat(cnt <= 2 * mean, BLK)[:N]
+    assert (~unsplit).any() and unsplit.any()
+    rows = torch.from_numpy(np.nonzero(unsplit)[0]).to(q.device)
+    assert torch.equal(o1[:, :, rows].view(torch.int16), o2[:, :, rows].view(torch.int16))
+    assert torch.equal(l1[:, :, rows], l2[:, :, rows])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_pass_path_random_masks(fa, causal):
+    """The path without a workspace (one workgroup per query block)."""
+    import torch
+
+    N, d = 700, 128
+    nb = -(-N // BLK)
+    mask = _heavy_mask(nb, 3)
+    q, k, v = random_inputs(23, (2, 2, N, d), "bf16", 3)
+    o, lse = fa.forward_block_sparse(dev(q), dev(k), dev(v), _mask_dev(mask), causal=causal, balance=False)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_block_sparse(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), mask, BLK,
+                                                   causal, 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl)
