@@ -254,3 +254,34 @@ def test_forward_is_deterministic_across_streams(fa):
     for o, lse in outs:
         assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
         assert torch.equal(lse, rl)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_magnitude_inputs(fa, causal):
+    """Inputs x8 (scores up to ~1e3 * scale): the running max jumps by far
+    more than the lazy-rescale threshold between tiles and exp() would
+    overflow without the max subtraction; forward and backward stay within
+    tolerance of the oracle relative to the inputs' scale."""
+    import torch
+
+    B, H, N, d = 1, 2, 700, 128
+    q, k, v, do = random_inputs(77, (B, H, N, d), "bf16", 4, mult=8.0)
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(tq, tk, tv, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    qf, kf, vf, gf = (fi.exact_f64(a) for a in (q, k, v, do))
+    ro, rl = oracle.attention_forward(qf, kf, vf, causal, scale)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    # O (up to ~35) and LSE (up to ~330) are far from unit scale: the bar for
+    # O is 1% of its largest magnitude plus its bf16 storage rounding
+    assert max_abs(host64(o), ro) <= 0.01 * np.abs(ro).max() + storage_floor(ro)
+    assert np.abs(host64(lse) - rl).max() <= TOL_LSE
+    ref = oracle.attention_backward(qf, kf, vf, gf, causal, scale)
+    # gradients at this scale are large: the bar is 2% of their largest
+    # magnitude plus their own bf16 storage rounding
+    for name, x, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        e = max_abs(host64(x), r)
+        bar = 0.02 * np.abs(r).max() + storage_floor(r)
+        assert e <= bar, f"{name}: {e:.3g} > {bar:.3g} (floor {storage_floor(r):.3g})"
