@@ -7,7 +7,8 @@
 //
 //  * prepare: each row of Q and K is multiplied by a random sign vector and
 //    by the Sylvester Hadamard matrix (float32 butterfly, widths 1, 2, ...,
-//    64; the 1/sqrt(128) of both is folded into the softmax scale as 1/128),
+//    64, each pair (a, b) -> (a + b, a - b); the 1/sqrt(128) of both is
+//    folded into the softmax scale as 1/128),
 //    then quantised to OCP E4M3 with one power-of-two scale per 32 elements
 //    (the smallest 2^t with amax <= 448 * 2^t, so nothing saturates).  V is
 //    quantised per column in blocks of 32 consecutive keys and stored
@@ -133,44 +134,54 @@ fp8_quant_rows_kernel(const uint16_t* __restrict__ X, const float* __restrict__ 
   reinterpret_cast<uint32_t*>(exps)[r] = ex;
 }
 
-// One thread per (batch*head, 32-key block, column); columns fastest, so
-// the reads of one key are coalesced across the wavefront.
+// One thread per (batch*head, 32-key block, 4 adjacent columns); column
+// groups fastest, so one wave-wide load of a key reads 512 contiguous bytes.
 __global__ void __launch_bounds__(256)
 fp8_quant_v_kernel(const uint16_t* __restrict__ V, uint8_t* __restrict__ v8, uint8_t* __restrict__ ve, int N, int Np,
                    long long total) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int c = (int)(idx % FD);
-  const long long rest = idx / FD;
+  constexpr int CG = FD / 4;                 // column groups per key
+  const int c0 = 4 * (int)(idx % CG);
+  const long long rest = idx / CG;
   const int nb32 = Np / 32;
   const int blk = (int)(rest % nb32);
   const long long bh = rest / nb32;
-  float x[32];
+  float x[4][32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int key = blk * 32 + i;
-    x[i] = key < N ? __uint_as_float((uint32_t)V[(bh * N + key) * FD + c] << 16) : 0.f;
+    u32x2 w = {0u, 0u};
+    if (key < N) w = *reinterpret_cast<const u32x2*>(V + (bh * N + key) * FD + c0);
+    x[0][i] = bf16_lo(w[0]);
+    x[1][i] = bf16_hi(w[0]);
+    x[2][i] = bf16_lo(w[1]);
+    x[3][i] = bf16_hi(w[1]);
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const int t = block_exponent(amax);
-  // Key 8j + 4g + i of the block goes to byte 16g + 4j + i.
-  float px[32];
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) px[16 * g + 4 * j + i] = x[8 * j + 4 * g + i];
-  uint32_t w[8];
-  quantize32(px, t, w);
   const int tile = blk >> 1, b = blk & 1;
   const long long tile_id = bh * (Np / 64) + tile;
-  u32x4* dst = reinterpret_cast<u32x4*>(v8 + (tile_id * FD + c) * 64 + 32 * b);
-  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-  ve[((tile_id * 2 + b) * 32 + (c & 31)) * 4 + (c >> 5)] = e8m0(t);
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[cc][i]));
+    const int t = block_exponent(amax);
+    // Key 8j + 4g + i of the block goes to byte 16g + 4j + i.
+    float px[32];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) px[16 * g + 4 * j + i] = x[cc][8 * j + 4 * g + i];
+    uint32_t w[8];
+    quantize32(px, t, w);
+    const int c = c0 + cc;
+    u32x4* dst = reinterpret_cast<u32x4*>(v8 + (tile_id * FD + c) * 64 + 32 * b);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    ve[((tile_id * 2 + b) * 32 + (c & 31)) * 4 + (c >> 5)] = e8m0(t);
+  }
 }
 
 // Block-scaled FP8 32x32x64 product; OPA/OPB pick the scale byte.
@@ -413,7 +424,7 @@ hipError_t launch_fp8_prepare(const uint16_t* q, const uint16_t* k, const uint16
                      L.Np, rows);
   hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rb), dim3(256), 0, stream, k, signs, base + L.k8, base + L.ke, N,
                      L.Np, rows);
-  const long long vt = (long long)BH * (L.Np / 32) * FD;
+  const long long vt = (long long)BH * (L.Np / 32) * (FD / 4);
   hipLaunchKernelGGL(fp8_quant_v_kernel, dim3((unsigned)((vt + 255) / 256)), dim3(256), 0, stream, v, base + L.v8,
                      base + L.ve, N, L.Np, vt);
   return hipGetLastError();
