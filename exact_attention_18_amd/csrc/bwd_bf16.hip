@@ -140,7 +140,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, g = lane >> 5;
   int bh, kb;
-  map_block_xcd(blockIdx.x, total, nkb, false, bh, kb);  // causal: low key blocks carry the most work
+  map_block(blockIdx.x, total, nkb, CAUSAL ? 2 : 0, bh, kb);  // causal: low key blocks carry the most work
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);

@@ -114,18 +114,32 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t lo, uint32_t hi) { return
 
 __device__ __forceinline__ uint32_t word_of(const u32x4& u, int i) { return u[i]; }
 
-// Workgroup id -> (batch*head, query block), with
-//  * all query blocks of one (batch, head) on one XCD: the dispatcher hands
-//    workgroup ids to the 8 XCDs round-robin, so consecutive logical ids are
-//    gathered from ids that share id % 8;
-//  * optionally the heaviest causal query blocks first (largest block index).
+// Workgroup id -> (batch*head, block).  The dispatcher hands workgroup ids
+// to the 8 XCDs round-robin (id % 8), each XCD with its own L2.
+//  * order 0 (every block the same work): logical ids are gathered from
+//    ids that share id % 8, so all blocks of one (batch, head) land on one
+//    XCD and its K/V stay in that XCD's L2;
+//  * order 1 / 2 (causal: the work grows with the block index / shrinks
+//    with it): block-major order, the heaviest block of every head first,
+//    so the last workgroups dispatched are the lightest and the tail stays
+//    short.  Id w takes head w % BH; when BH is a multiple of 8 every head
+//    still stays on one XCD.
+__device__ __forceinline__ void map_block(int w, int total, int nq, int order, int& bh, int& blk) {
+  if (order == 0) {
+    const int per = total >> 3, rem = total & 7;
+    const int x = w & 7, loc = w >> 3;
+    const int logical = x * per + (x < rem ? x : rem) + loc;
+    bh = logical / nq;
+    blk = logical - bh * nq;
+    return;
+  }
+  const int BH = total / nq;
+  const int i = w / BH;
+  bh = w - i * BH;
+  blk = order == 1 ? nq - 1 - i : i;
+}
 __device__ __forceinline__ void map_block_xcd(int w, int total, int nq, bool heavy_first, int& bh, int& qb) {
-  const int per = total >> 3, rem = total & 7;
-  const int x = w & 7, loc = w >> 3;
-  const int logical = x * per + (x < rem ? x : rem) + loc;
-  bh = logical / nq;
-  const int i = logical - bh * nq;
-  qb = heavy_first ? nq - 1 - i : i;
+  map_block(w, total, nq, heavy_first ? 1 : 0, bh, qb);
 }
 
 }  // namespace fa
