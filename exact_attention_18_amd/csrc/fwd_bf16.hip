@@ -90,6 +90,48 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* stage
   }
 }
 
+// Online-softmax bookkeeping for one wave's 64-key tile of S^T (element r of
+// s[kb] is key 32*kb + 8*(r/4) + 4*g + r%4): optional mask (keys past `lim`
+// get -inf), row max, and the lazy rescale of the reference max m, the row
+// sum and the output accumulators.
+template <int D, bool MASK>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D / 32], float& m, float& lsum, float c,
+                                               int lim) {
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+  }
+  // Row max as a shallow tree (v_max3), not a 32-long dependent chain.
+  // max_nan (NaN-propagating maximum) lowers to v_maximum3_f32 without the
+  // operand canonicalisation that fmaxf needs in IEEE mode.
+  float m8[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h;
+      const float a = max_nan(max_nan(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
+      const float b = max_nan(max_nan(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
+      m8[2 * kb + h] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
+    }
+  float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
+  mx = max_halves(mx) * c;  // c > 0: the scaled row max over the tile (or -inf)
+
+  // Raise the reference max only when some row's tile max exceeds it by
+  // more than TAU; otherwise p stays below 2^TAU and nothing is rescaled.
+  if (__any(mx > m + TAU)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2_hw(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+  }
+}
+
 // One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax update,
 // O^T += V^T P^T.  MASK selects the variant for tiles that straddle the
 // diagonal or the end of N; `lim` is the largest visible key offset within
@@ -125,39 +167,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 
-  if (MASK) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
-  }
-  // Row max as a shallow tree (v_max3), not a 32-long dependent chain.
-  // max_nan (NaN-propagating maximum) lowers to v_maximum3_f32 without the
-  // operand canonicalisation that fmaxf needs in IEEE mode.
-  float m8[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 8 * h;
-      const float a = max_nan(max_nan(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
-      const float b = max_nan(max_nan(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
-      m8[2 * kb + h] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
-    }
-  float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
-  mx = max_halves(mx) * c;  // c > 0: the scaled row max over the tile (or -inf)
-
-  // Raise the reference max only when some row's tile max exceeds it by
-  // more than TAU; otherwise p stays below 2^TAU and nothing is rescaled.
-  if (__any(mx > m + TAU)) {
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2_hw(m - mn);
-    m = mn;
-    lsum *= alpha;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-  }
+  softmax_update<D, MASK>(s, oacc, m, lsum, c, lim);
 
   // Exponentials of block (kb, t) then its four PV products, so the matrix
   // cores can run block b while the VALU computes block b+1.
@@ -332,13 +342,321 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense forward, d = 128: two wave groups in alternation.
+//
+// The page "FlashAttention-3 — FlashAttention-3" (section on overlapping the
+// softmax with the matrix products) describes two warpgroups that take turns:
+// while one runs its matrix products, the other runs its softmax.  On gfx950
+// the same idea maps onto the two waves that share a SIMD.  A workgroup of 8
+// waves owns 256 queries; waves w and w+4 run on the same SIMD (the
+// dispatcher places the waves of a workgroup on the 4 SIMDs in turn), group 0
+// is waves 0-3 and group 1 waves 4-7.  Each wave alternates
+//   matrix phase k:  S(k) = K(k) Q^T (64 keys) and O^T += V(k-1)^T P(k-1)^T
+//   softmax phase k: mask, row max and lazy rescale on S(k), P(k) = exp2(...)
+// and the groups run them one phase apart, with a workgroup barrier between
+// phases: in every phase one wave per SIMD keeps the matrix core busy while
+// the other wave's softmax runs on the vector ALU.  Per query the arithmetic
+// and its order are those of fwd_bf16_kernel (same tiles in the same order,
+// same lazy rescale, same sums), so the results are identical.
+//
+// Phase pair k: group 0 runs matrix phase k then softmax phase k; group 1
+// runs softmax phase k-1 then matrix phase k.  Tiles K(k+1) and V(k) are
+// written to LDS during pair k, each group storing half of them in its
+// softmax phase, from registers it fetched from HBM one pair earlier; their
+// slots held K(k-1) and V(k-2), whose last reads were in pair k-1.  The
+// barriers are also scheduling fences, so no instruction migrates from one
+// phase into the next.
+constexpr int PP_BR = 256;              // queries per workgroup
+constexpr int PP_NT = 512;              // 8 waves
+constexpr int PP_MIN_CAUSAL_N = 2049;   // shorter causal problems use fwd_bf16_kernel
+
+template <int D>
+struct PpLds {
+  static constexpr int KS = D + FA_FWD_KPAD;
+  static constexpr int VS = D + FA_FWD_VPAD;
+  static constexpr int K_ELEMS = BC * KS;
+  static constexpr int V_ELEMS = BC * VS;
+  static constexpr int V0 = 2 * K_ELEMS;                   // K slots 0, 1, then V slots 0, 1
+  static constexpr int ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;
+  static constexpr int CPR = D / 8;                        // 16-byte chunks per row
+  static constexpr int CPT = BC * CPR / PP_NT;             // chunks per thread for a whole tile
+  static constexpr int HALF = BC * CPR / 2;                // chunks in half a tile
+};
+
+// HBM -> registers and registers -> LDS for chunks [first, first + CPT * step)
+// of a 64-row tile, `step` apart (a whole tile: first = tid, step = 512; a
+// group's half: first = half * HALF + thread-in-group, step = 256).  Rows at
+// or past N read as zero (buffer bounds).
+template <int D>
+__device__ __forceinline__ void pp_load(u32x4 (&r)[PpLds<D>::CPT], __amdgpu_buffer_rsrc_t rs, int kv0, int first,
+                                        int step) {
+  using L = PpLds<D>;
+#pragma unroll
+  for (int i = 0; i < L::CPT; ++i) {
+    const int c = first + step * i;
+    r[i] = buf_load16(rs, (uint32_t)(((kv0 + c / L::CPR) * D + (c % L::CPR) * 8) * 2));
+  }
+}
+template <int D, int STRIDE>
+__device__ __forceinline__ void pp_store(const u32x4 (&r)[PpLds<D>::CPT], uint16_t* dst, int first, int step) {
+  using L = PpLds<D>;
+#pragma unroll
+  for (int i = 0; i < L::CPT; ++i) {
+    const int c = first + step * i;
+    *reinterpret_cast<u32x4*>(dst + (c / L::CPR) * STRIDE + (c % L::CPR) * 8) = r[i];
+  }
+}
+
+// Matrix phase: S = K Q^T on the tile at Ks (QK), then O^T += V^T P^T on
+// the tile at Vs with P packed in pw (PV).
+template <int D, bool QK, bool PV>
+__device__ __forceinline__ void pp_matrix(const uint16_t* Ks, const uint16_t* Vs, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&s)[2], const u32x4 (&pw)[4], f32x16 (&oacc)[D / 32],
+                                          int lane) {
+  using L = PpLds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  const int l32 = lane & 31, g = lane >> 5;
+  if (QK) {
+    const uint16_t* krow = Ks + l32 * L::KS + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma32(bf16x8_from(*reinterpret_cast<const u32x4*>(krow + kb * 32 * L::KS + ks * 16)), qf[ks],
+                       ks == 0 ? f32x16{} : s[kb]);
+  }
+  if (PV) {
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint16_t* vp = Vs + ((b >> 1) * 32 + 16 * (b & 1) + tr_row) * L::VS + tr_col;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        oacc[db] = mfma32(bf16x8_from(lds_read_tr16(vp + db * 32), lds_read_tr16(vp + 8 * L::VS + db * 32)),
+                          __builtin_bit_cast(bf16x8, pw[b]), oacc[db]);
+    }
+  }
+  // Eight LDS reads (mask 0x100) ahead of the products (mask 0x008), then
+  // one or two reads per product.
+  constexpr int NM = (QK ? 2 * KSTEPS : 0) + (PV ? 4 * DB : 0);
+  constexpr int NR = (QK ? 2 * KSTEPS : 0) + (PV ? 8 * DB : 0);
+  constexpr int AHEAD = NR < 8 ? NR : 8;
+  constexpr int R2 = NR - AHEAD - NM > 0 ? NR - AHEAD - NM : 0;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < R2)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// Softmax phase: softmax_update on S, then P = exp2(c s - m) packed to bf16
+// into pw (block b = (kb, t) holds keys 32 kb + 16 t + ...), row sum into
+// lsum, in the order tile_step uses.
+template <int D, bool MASK>
+__device__ __forceinline__ void pp_softmax(f32x16 (&s)[2], u32x4 (&pw)[4], f32x16 (&oacc)[D / 32], float& m,
+                                           float& lsum, float c, int lim) {
+  softmax_update<D, MASK>(s, oacc, m, lsum, c, lim);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float ps[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * t + 2 * e;
+        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
+        ps[e] = p0 + p1;
+        pw[2 * kb + t][e] = pack_bf16x2(p0, p1);
+      }
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+}
+
+// Workgroup barrier that is also a scheduling fence.
+__device__ __forceinline__ void pp_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(PP_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+              uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c) {
+  constexpr int D = 128;
+  using L = PpLds<D>;
+  constexpr int KSTEPS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int gt = tid & (PP_NT / 2 - 1);   // thread within the group
+  const int l32 = lane & 31, g = lane >> 5;
+  int bh, qb;
+  map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
+  const size_t base = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+  const int q0 = qb * PP_BR;
+  // The two waves of a SIMD take adjacent 32-query slices, so both groups
+  // meet the causal diagonal in the same tiles.
+  const int qw = q0 + 64 * (wave & 3) + 32 * grp;
+  const int myq = qw + l32;
+
+  bf16x8 qf[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    qf[ks] = bf16x8_from(buf_load16(qrs, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2)));
+
+  const int kv_end = CAUSAL ? min(N, q0 + PP_BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  // Last tile this wave sees, and the first one that needs the mask (it has
+  // a key past one of the wave's queries, or past N).
+  const int last_w = CAUSAL ? min(qw + 31, N - 1) / BC : ntiles - 1;
+  const int first_mask_w = min(CAUSAL ? (qw + 1) / BC : ntiles, N / BC);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
+  f32x16 s[2];
+  u32x4 pw[4];
+  u32x4 rk[L::CPT], rv[L::CPT];
+  auto kslot = [&](int j) { return smem + (j & 1) * L::K_ELEMS; };
+  auto vslot = [&](int j) { return smem + L::V0 + (j & 1) * L::V_ELEMS; };
+  auto fetch = [&](int k) {   // this group's half of K(k+1) and V(k), HBM -> registers
+    if (k + 1 < ntiles) pp_load<D>(rk, krs, (k + 1) * BC, grp * L::HALF + gt, PP_NT / 2);
+    if (k < ntiles) pp_load<D>(rv, vrs, k * BC, grp * L::HALF + gt, PP_NT / 2);
+  };
+  auto store = [&](int k) {   // ... registers -> LDS
+    if (k + 1 < ntiles) pp_store<D, L::KS>(rk, kslot(k + 1), grp * L::HALF + gt, PP_NT / 2);
+    if (k < ntiles) pp_store<D, L::VS>(rv, vslot(k), grp * L::HALF + gt, PP_NT / 2);
+  };
+  // Softmax phase i; a tile the wave does not see (causal) gives P = 0.
+  auto softmax = [&](int i, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (i > last_w) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) pw[b] = u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+    const int lim = MASK ? (CAUSAL ? min(myq, N - 1) : N - 1) - i * BC - 4 * g : 0;
+    pp_softmax<D, MASK>(s, pw, oacc, m, lsum, c, lim);
+  };
+  auto matrix = [&](int k, auto qk_tag, auto pv_tag) {
+    pp_matrix<D, decltype(qk_tag)::value, decltype(pv_tag)::value>(kslot(k), vslot(k - 1), qf, s, pw, oacc, lane);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  pp_load<D>(rk, krs, 0, tid, PP_NT);   // K(0), whole tile
+  pp_store<D, L::KS>(rk, kslot(0), tid, PP_NT);
+  fetch(0);
+  pp_sync();
+
+  // Pairs 1 .. ntiles-1 run the full matrix phase; the pairs whose softmax
+  // needs no mask come first.  Both groups pass the same number of barriers.
+  const int k_mask = max(1, min(grp == 0 ? first_mask_w : first_mask_w + 1, ntiles));
+  if (grp == 0) {
+    matrix(0, T{}, F{});
+    pp_sync();
+    if (0 < first_mask_w) softmax(0, F{}); else softmax(0, T{});
+    store(0);
+    fetch(1);
+    pp_sync();
+    int k = 1;
+    for (; k < k_mask; ++k) {
+      matrix(k, T{}, T{});
+      pp_sync();
+      softmax(k, F{});
+      store(k);
+      fetch(k + 1);
+      pp_sync();
+    }
+    for (; k < ntiles; ++k) {
+      matrix(k, T{}, T{});
+      pp_sync();
+      softmax(k, T{});
+      store(k);
+      fetch(k + 1);
+      pp_sync();
+    }
+    matrix(ntiles, F{}, T{});
+    pp_sync();
+    pp_sync();
+  } else {
+    store(0);
+    fetch(1);
+    pp_sync();
+    matrix(0, T{}, F{});
+    pp_sync();
+    int k = 1;
+    for (; k < k_mask; ++k) {
+      softmax(k - 1, F{});
+      store(k);
+      fetch(k + 1);
+      pp_sync();
+      matrix(k, T{}, T{});
+      pp_sync();
+    }
+    for (; k < ntiles; ++k) {
+      softmax(k - 1, T{});
+      store(k);
+      fetch(k + 1);
+      pp_sync();
+      matrix(k, T{}, T{});
+      pp_sync();
+    }
+    if (ntiles - 1 < first_mask_w) softmax(ntiles - 1, F{}); else softmax(ntiles - 1, T{});
+    pp_sync();
+    matrix(ntiles, F{}, T{});
+    pp_sync();
+  }
+
+  const float ltot = sum_halves(lsum);
+  const float inv = ltot > 0.f ? rcp_hw(ltot) : 0.f;
+  if (myq < N) {
+    uint16_t* orow = O + base + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
+                   pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
+      }
+    if (g == 0) LSE[(size_t)bh * N + myq] = ltot > 0.f ? (m + log2_hw(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
 template <int D, bool CAUSAL, bool SPARSE = false>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                   int BH, int N, float scale, hipStream_t stream, const uint8_t* bmask = nullptr) {
+  // Buffer offsets are 32-bit: one head of K or V must stay below 2 GiB.
+  if ((long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  if constexpr (D == 128 && !SPARSE) {
+    if (!CAUSAL || N >= PP_MIN_CAUSAL_N) {
+      const int nqb = (N + PP_BR - 1) / PP_BR;
+      const long long total = (long long)BH * nqb;
+      if (total > 0x7fffffffLL) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)total), dim3(PP_NT), 0, stream, q, k, v, o, lse, N,
+                         nqb, (int)total, score_coef(scale));
+      return hipGetLastError();
+    }
+  }
   const int nqb = (N + BR - 1) / BR;
   const long long total = (long long)BH * nqb;
-  // Buffer offsets are 32-bit: one head of K or V must stay below 2 GiB.
-  if (total > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  if (total > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)total), dim3(NT), 0, stream,
                      q, k, v, o, lse, N, nqb, (int)total, score_coef(scale), bmask);
   return hipGetLastError();

@@ -84,6 +84,29 @@ def test_bf16_forward_small(fa, N, d, causal):
     _check_fwd(fa, "bf16", 2, 3, N, d, causal, seed=N)
 
 
+@pytest.mark.parametrize("N", [2049, 2113, 2300, 2623, 3000])
+def test_bf16_forward_causal_above_2048(fa, N):
+    """Causal d = 128 problems longer than 2048 keys take the two-group
+    kernel (256-query blocks): ragged ends against its 64-key tiles and
+    256-query blocks, and a diagonal that crosses the two groups' slices."""
+    _check_fwd(fa, "bf16", 1, 2, N, 128, True, seed=N)
+
+
+@pytest.mark.parametrize("N", [2049, 2300])
+def test_two_group_forward_equals_one_group_rows(fa, N):
+    """Per query the two-group kernel does the one-group kernel's arithmetic
+    in the same order, so the first 2048 queries of a causal N > 2048
+    problem (which see only the first 2048 keys) are bit-identical to the
+    causal N = 2048 problem on the same rows."""
+    import torch
+
+    q, k, v = random_inputs(7, (1, 2, N, 128), "bf16", 3)
+    o1, l1 = _run_fwd(fa, q, k, v, True, 128 ** -0.5)
+    o2, l2 = _run_fwd(fa, q[:, :, :2048].copy(), k[:, :, :2048].copy(), v[:, :, :2048].copy(), True, 128 ** -0.5)
+    assert torch.equal(o1[:, :, :2048].view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1[:, :, :2048], l2)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", SMALL_N)
