@@ -33,6 +33,11 @@ namespace {
 
 constexpr int NT = 256;
 
+// Waves per SIMD: at d = 64 both kernels fit 168 VGPRs and ~37 KB of LDS, so
+// three workgroups share a CU (measured +8% over two); at d = 128 two.
+template <int D>
+constexpr int bwd_waves_per_simd() { return D == 64 ? 3 : 2; }
+
 // Row stride (elements) of a tile that is read both with 16-byte row reads
 // (32 rows, one column block) and with the transpose read (4 rows x 32
 // bytes per 16 lanes): 48 bytes (d=128) or 144 bytes (d=64) past a multiple
@@ -125,7 +130,7 @@ struct DkdvLds {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const float* __restrict__ LSE,
                 const uint16_t* __restrict__ dO, const float* __restrict__ delta,
@@ -298,7 +303,7 @@ struct DqLds {
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const float* __restrict__ LSE,
               const uint16_t* __restrict__ dO, const float* __restrict__ delta,
