@@ -354,6 +354,26 @@ def main():
                            "tflops": round(dw.flops() / (dms * 1e-3) / 1e12, 2)})
             del dq_, dk_, dv_, do_, dl_, dws
 
+    # Backward with a stored dS (fa_backward_stored_ds, O(N^2) workspace) on
+    # the step's own tensors, beside fa_backward on the same tensors: both
+    # whole backward passes (row-dot pre-pass included), same FLOP count.
+    stored_ds = []
+    if w.backward and not args.no_headline:
+        sws_bytes = fa.fa_backward_stored_ds_workspace_size(B, H, N, d)
+        if sws_bytes:
+            sws = torch.empty(sws_bytes, dtype=torch.uint8, device=dev)
+            args_b = (P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"], P["dk"], P["dv"], B, H, N, d,
+                      causal, scale)
+            sms_ = time_launches(lambda: checked(fa.fa_backward_stored_ds(*args_b, sws.data_ptr(), sws_bytes, sp),
+                                                 "backward_stored_ds"))
+            bms_ = time_launches(lambda: checked(fa.fa_backward(*args_b, P["ws"], ws_bytes, sp), "backward"))
+            bf = w.bwd_flops()
+            stored_ds.append({"workload": w.name, "entry": "fa_backward_stored_ds", "ms": round(sms_, 4),
+                              "tflops": round(bf / (sms_ * 1e-3) / 1e12, 1), "workspace_MiB": round(sws_bytes / 2**20),
+                              "fa_backward_ms": round(bms_, 4),
+                              "fa_backward_tflops": round(bf / (bms_ * 1e-3) / 1e12, 1)})
+            del sws
+
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
 
@@ -390,6 +410,7 @@ def main():
         "block_sparse_forward": block_sparse,
         "decode": decode,
         "fp8_forward": fp8,
+        "backward_stored_ds": stored_ds,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import FA_OK, FaLibraryMissing, load  # noqa: F401
+from ._lib import FA_ERR_UNSUPPORTED, FA_OK, FaLibraryMissing, load  # noqa: F401
 
 __all__ = [
     "FaError",
@@ -36,6 +36,8 @@ __all__ = [
     "fa_backward_dkdv",
     "fa_backward_dq",
     "fa_backward_workspace_size",
+    "fa_backward_stored_ds",
+    "fa_backward_stored_ds_workspace_size",
     "fa_status_string",
     "fa_abi_version",
     "forward",
@@ -45,6 +47,7 @@ __all__ = [
     "forward_fp8",
     "DECODE_MAX_QUERIES",
     "backward",
+    "backward_stored_ds",
     "BLOCK_SPARSE_BLOCK",
 ]
 
@@ -133,6 +136,16 @@ def fa_backward_f32(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, 
 
 def fa_backward_workspace_size(B, H, N, d) -> int:
     return int(_call("fa_backward_workspace_size", B, H, N, d))
+
+
+def fa_backward_stored_ds_workspace_size(B, H, N, d) -> int:
+    return int(_call("fa_backward_stored_ds_workspace_size", B, H, N, d))
+
+
+def fa_backward_stored_ds(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes,
+                          stream) -> int:
+    return _call("fa_backward_stored_ds", q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, int(causal),
+                 float(scale), ws, ws_bytes, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -327,6 +340,35 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv
+
+
+def backward_stored_ds(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
+    """dQ, dK, dV like ``backward`` (bf16 only), through fa_backward_stored_ds:
+    the dK/dV pass stores dS in a B*H*N*N-sized workspace and dQ is computed
+    from it (O(N^2) workspace instead of a recompute)."""
+    import torch
+
+    f32 = _check([q, k, v, o, do], ["q", "k", "v", "o", "do"])
+    if f32:
+        raise TypeError("backward_stored_ds takes bfloat16 tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    need = fa_backward_stored_ds_workspace_size(B, H, N, d)
+    if need == 0:
+        raise FaError(FA_ERR_UNSUPPORTED)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_backward_stored_ds(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal,
+                               scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

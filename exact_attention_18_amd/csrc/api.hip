@@ -360,6 +360,41 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                        scale, workspace, workspace_bytes, stream, true);
 }
 
+size_t fa_backward_stored_ds_workspace_size(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  const long long nk = (N + 127LL) / 128 * 128;
+  if ((N + 128LL) * nk * 2 >= (1LL << 31)) return 0;
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  const unsigned long long ds = bh * (unsigned long long)N * (unsigned long long)nk * 2ULL;
+  if (ds / 2ULL / (unsigned long long)nk / (unsigned long long)N != bh || ds > (1ULL << 50)) return 0;
+  return fa_backward_workspace_size(B, H, N, d) + (size_t)ds;
+}
+
+int fa_backward_stored_ds(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                          int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_backward_stored_ds_workspace_size(B, H, N, d);
+  if (need == 0) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(lse, lb), span(dO, tb)};
+  const void* inp[6] = {q, k, v, o, lse, dO};
+  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
+  const void* outp[4] = {dq, dk, dv, workspace};
+  st = check_buffers(ins, inp, 6, outs, outp, 4);
+  if (st != FA_OK) return st;
+  float* delta = static_cast<float*>(workspace);
+  uint16_t* ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + fa_backward_workspace_size(B, H, N, d));
+  return hip_status(fa::launch_bwd_stored_ds_bf16(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, delta, ds,
+      static_cast<hipStream_t>(stream)));
+}
+
 int fa_backward_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
                     const float* dO, float* dq, float* dk, float* dv, int B, int H, int N, int d,
                     int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {

@@ -20,6 +20,15 @@
 // orientation come from the LDS transpose read.  Tiles are double-buffered:
 // tile i+1 is fetched into registers while tile i is computed.
 //
+// Stored-dS variant (a caller workspace of B*H*N*Nk bf16, Nk = N rounded up
+// to 128): the dK/dV kernel also writes dS, row q holding dS[q][k] for every
+// key k of the workgroup's block (0 where masked), and dQ = scale * dS K is
+// then one product per tile read back from it, instead of the dQ kernel's
+// recompute of S and dP.  It trades the O(N) memory of the two-kernel path
+// for O(N^2).  Within each group of 16 keys the columns are stored in the
+// slot order of the transpose read (ds_column), so that a 16-byte row read
+// of dS is the B operand matching a transpose-read K operand.
+//
 // Ragged N needs no masks here: rows past N read as zero (buffer loads), a
 // zero key row contributes nothing to dQ, a query past N has LSE = +inf so
 // its P is 0, and results for keys or queries past N are never stored.
@@ -91,6 +100,13 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int row0, int
   return bf16x8_from(lds_read_tr16(p), lds_read_tr16(p + 8 * STRIDE));
 }
 
+// Column of key k in a stored dS row: bits 2 and 3 of k swapped, so that the
+// 8 keys a lane half takes from the transpose read (4g + 0..3 and
+// 8 + 4g + 0..3 of each 16) sit in 8 consecutive columns 8g + 0..7.
+__device__ __forceinline__ int ds_column(int k) {
+  return (k & ~15) | (k & 3) | ((k & 8) >> 1) | ((k & 4) << 1);
+}
+
 // Accumulator elements r = 8t .. 8t+7 of `x` as one bf16 operand.
 __device__ __forceinline__ bf16x8 acc_to_operand(const f32x16& x, int t) {
   u32x4 u = {pack_bf16x2(x[8 * t + 0], x[8 * t + 1]), pack_bf16x2(x[8 * t + 2], x[8 * t + 3]),
@@ -129,13 +145,14 @@ struct DkdvLds {
   static constexpr int ELEMS = V_ELEMS + 2 * STAGE;
 };
 
-template <int D, bool CAUSAL>
+// WRITE_DS: also store dS (bf16, row stride Nk) for the stored-dS dQ.
+template <int D, bool CAUSAL, bool WRITE_DS>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const float* __restrict__ LSE,
                 const uint16_t* __restrict__ dO, const float* __restrict__ delta,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkb, int total,
-                float c, float scale) {
+                float c, float scale, uint16_t* __restrict__ dS, int Nk) {
   using L = DkdvLds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
@@ -155,6 +172,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int k0 = kb * KV_BLK;
   const int kw = k0 + wave * 32;
   const int myk = kw + l32;
+  // dS column of this lane's key, rows 4g + ... of each query tile; rows
+  // past N lie past the end of the head's buffer and are dropped.
+  const __amdgpu_buffer_rsrc_t dsr =
+      make_rsrc(WRITE_DS ? dS + (size_t)bh * N * Nk : dS, WRITE_DS ? (uint32_t)N * Nk * 2 : 0u);
+  const uint32_t ds_off = WRITE_DS ? (uint32_t)(4 * g * Nk + ds_column(myk)) * 2 : 0u;
+  // element r of an accumulator is query row 8(r/4) + 4g + r%4 of the tile
+  auto ds_row = [&](int qt0, int r) { return (qt0 + 8 * (r >> 2) + (r & 3)) * Nk * 2; };
 
   // This lane's K row as the B operand of S = Q K^T (rows past N read as zero).
   bf16x8 kf[KSTEPS];
@@ -255,6 +279,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int t = 0; t < 2; ++t) {
         const bf16x8 pb = acc_to_operand(s, t);
         const bf16x8 dsb = acc_to_operand(dp, t);
+        if constexpr (WRITE_DS) {
+          // word e of dsb holds elements 8t + 2e (low half) and 8t + 2e + 1
+          const u32x4 w = __builtin_bit_cast(u32x4, dsb);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[e] & 0xffffu), dsr, ds_off,
+                                                  ds_row(qt0, 8 * t + 2 * e), 0);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w[e] >> 16), dsr, ds_off,
+                                                  ds_row(qt0, 8 * t + 2 * e + 1), 0);
+          }
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           dvt[db] = mfma32(tr_operand<L::QS>(Gs, 0, 32 * db, t, lane), pb, dvt[db]);
@@ -272,6 +307,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         }
         __builtin_amdgcn_sched_group_barrier(0x008, AH / 2, 0);
       }
+    }
+    else if constexpr (WRITE_DS) {
+      // every query of the tile precedes this wave's keys: dS = 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)0, dsr, ds_off, ds_row(qt0, r), 0);
     }
     if (i + 1 < ntiles) put(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
     __syncthreads();
@@ -405,6 +446,81 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (myq < N) store_acc_row<D>(dQ + base + (size_t)myq * D, dqt, scale, g);
 }
 
+// ---------------------------------------------------------------- dQ from stored dS
+template <int D>
+struct DqDsLds {
+  static constexpr int KS = D + 32;        // K tile, transpose reads only
+  static constexpr int ELEMS = 2 * K_TILE * KS;
+};
+
+// dQ = scale * dS K from the stored dS: one workgroup per (batch*head, 128
+// queries), each wave 32 queries, key tiles of 64 (causal: up to the
+// diagonal, where the stored dS is already 0 past each query).  dQ^T +=
+// K^T dS^T: the K^T operand comes from the LDS transpose read, the dS^T
+// operand is a 16-byte read of this lane's dS row (the stored column order
+// matches the transpose read's key slots), straight from HBM: no other wave
+// needs those rows.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_dq_from_ds_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ dS,
+                      uint16_t* __restrict__ dQ, int N, int Nk, int nqb, int total, float scale) {
+  using L = DqDsLds<D>;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  int bh, qb;
+  map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
+  const size_t base = (size_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, (uint32_t)N * D * 2);
+  // Rows (queries) past N read as zero; keys past N meet zero K rows.
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(dS + (size_t)bh * N * Nk, (uint32_t)N * Nk * 2);
+  const int q0 = qb * Q_BLK;
+  const int myq = q0 + wave * 32 + l32;
+  const uint32_t srow = (uint32_t)(myq * Nk + 8 * g) * 2;
+
+  f32x16 dqt[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqt[i] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(N, q0 + Q_BLK) : N;
+  const int ntiles = (kv_end + K_TILE - 1) / K_TILE;
+  Rows<K_TILE, D> krows;
+  bf16x8 sf[2][4];   // this lane's dS for the current and the next tile
+  auto load_s = [&](bf16x8 (&dst)[4], int kv0) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) dst[ks] = bf16x8_from(buf_load16(srs, srow + (uint32_t)(kv0 + 16 * ks) * 2));
+  };
+  krows.load(krs, 0, tid);
+  load_s(sf[0], 0);
+  krows.template store<L::KS>(smem, tid);
+  __syncthreads();
+
+  auto step = [&](int j, bf16x8 (&cur)[4], bf16x8 (&nxt)[4]) {
+    const uint16_t* Ks = smem + (j & 1) * K_TILE * L::KS;
+    if (j + 1 < ntiles) {
+      krows.load(krs, (j + 1) * K_TILE, tid);
+      load_s(nxt, (j + 1) * K_TILE);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqt[db] = mfma32(tr_operand<L::KS>(Ks, (ks >> 1) * 32, 32 * db, ks & 1, lane), cur[ks], dqt[db]);
+    if (j + 1 < ntiles) krows.template store<L::KS>(smem + ((j + 1) & 1) * K_TILE * L::KS, tid);
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, sf[0], sf[1]);
+    step(j + 1, sf[1], sf[0]);
+  }
+  if (j < ntiles) step(j, sf[0], sf[1]);
+  if (myq < N) store_acc_row<D>(dQ + base + (size_t)myq * D, dqt, scale, g);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
                        const uint16_t* dO, const float* delta, uint16_t* dk, uint16_t* dv, int BH,
@@ -412,8 +528,30 @@ hipError_t launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   const int nkb = (N + KV_BLK - 1) / KV_BLK;
   const long long tk = (long long)BH * nkb;
   if (tk > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)tk), dim3(NT), 0, stream, q, k, v, lse,
-                     dO, delta, dk, dv, N, nkb, (int)tk, score_coef(scale), scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3((unsigned)tk), dim3(NT), 0, stream, q, k, v,
+                     lse, dO, delta, dk, dv, N, nkb, (int)tk, score_coef(scale), scale, nullptr, 0);
+  return hipGetLastError();
+}
+
+// Stored-dS backward after the row-dot pre-pass: dK/dV writing dS, then dQ
+// from it.  ds holds BH * N * Nk bf16 with Nk = N rounded up to 128.
+template <int D, bool CAUSAL>
+hipError_t launch_stored_ds(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                            const uint16_t* dO, const float* delta, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                            uint16_t* ds, int BH, int N, float scale, hipStream_t stream) {
+  const int Nk = (N + KV_BLK - 1) / KV_BLK * KV_BLK;
+  const int nkb = Nk / KV_BLK, nqb = (N + Q_BLK - 1) / Q_BLK;
+  const long long tk = (long long)BH * nkb, tq = (long long)BH * nqb;
+  // buffer offsets are 32-bit: rows up to N + 127 of one head's dS below 2 GiB
+  if (tk > 0x7fffffffLL || tq > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31) ||
+      (long long)(N + Q_BLK) * Nk * 2 >= (1LL << 31))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3((unsigned)tk), dim3(NT), 0, stream, q, k, v, lse,
+                     dO, delta, dk, dv, N, nkb, (int)tk, score_coef(scale), scale, ds, Nk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_from_ds_kernel<D, CAUSAL>), dim3((unsigned)tq), dim3(NT), 0, stream, k, ds, dq, N,
+                     Nk, nqb, (int)tq, scale);
   return hipGetLastError();
 }
 
@@ -454,6 +592,21 @@ hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16
   if (d == 128)
     return causal ? launch_dq<128, true>(q, k, v, lse, dO, delta, dq, BH, N, scale, stream)
                   : launch_dq<128, false>(q, k, v, lse, dO, delta, dq, BH, N, scale, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_stored_ds_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
+                                     uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal, float scale,
+                                     float* delta, uint16_t* ds, hipStream_t stream) {
+  hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
+  if (e != hipSuccess) return e;
+  if (d == 64)
+    return causal ? launch_stored_ds<64, true>(q, k, v, lse, dO, delta, dq, dk, dv, ds, BH, N, scale, stream)
+                  : launch_stored_ds<64, false>(q, k, v, lse, dO, delta, dq, dk, dv, ds, BH, N, scale, stream);
+  if (d == 128)
+    return causal ? launch_stored_ds<128, true>(q, k, v, lse, dO, delta, dq, dk, dv, ds, BH, N, scale, stream)
+                  : launch_stored_ds<128, false>(q, k, v, lse, dO, delta, dq, dk, dv, ds, BH, N, scale, stream);
   return hipErrorInvalidValue;
 }
 

@@ -61,6 +61,13 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
                            float scale, float* delta, hipStream_t stream);
 
+// Stored-dS backward: row-dot pre-pass into delta, dK/dV writing dS into ds
+// (BH * N * Nk bf16, Nk = N rounded up to 128), then dQ from dS.
+hipError_t launch_bwd_stored_ds_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
+                                     uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal, float scale,
+                                     float* delta, uint16_t* ds, hipStream_t stream);
+
 hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* lse, const uint16_t* dO, const float* delta,
                                 uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 enum fa_status {
   FA_OK = 0,
@@ -238,6 +238,31 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse
 /* Bytes of workspace fa_backward and fa_backward_f32 need for these sizes
  * (0 if a size is not positive).  Pure host function. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward with a stored dS (bf16 only): the outputs of fa_backward, from a
+ * larger workspace.  The dK/dV pass also writes dS = P * (dP - delta),
+ * rounded to bf16, into the workspace, and dQ = scale * dS K is then one
+ * matrix product per tile read back from it, where fa_backward's second pass
+ * recomputes S and dP.  The pages' backward recomputes instead of storing
+ * (page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の実践的
+ * エンジニアリング", section 「タイリング（Tiling）と再計算（Recomputation）の仕組み」);
+ * this entry point gives up that O(N) memory for O(N^2) workspace.
+ *   Arguments: as fa_backward, with
+ *   workspace: at least fa_backward_stored_ds_workspace_size(B, H, N, d)
+ *     bytes, 16-byte aligned, contents on entry ignored: the fa_backward
+ *     workspace followed by B*H*N*Nk bf16 (Nk = N rounded up to 128).
+ *   dK and dV are bit-identical to fa_backward's.  dQ agrees with it to
+ *   rounding: both multiply bf16-rounded dS by K, but the dS values come from
+ *   two different evaluations of S and dP.  Deterministic (no atomics).
+ *   Problems whose dS for one (batch, head) reaches 2 GiB
+ *   ((N + 128) * Nk * 2 >= 2^31) are rejected with FA_ERR_UNSUPPORTED.
+ */
+size_t fa_backward_stored_ds_workspace_size(int B, int H, int N, int d);
+int fa_backward_stored_ds(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                          int B, int H, int N, int d, int causal, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* float32 debug twins of fa_forward / fa_backward: same arguments, same
  * layouts and semantics, float32 storage and arithmetic throughout. */
