@@ -131,8 +131,10 @@ __device__ __forceinline__ void store_acc_row(uint16_t* __restrict__ dst_row, co
 }
 
 // ---------------------------------------------------------------- dK / dV
-constexpr int KV_BLK = 128;   // keys per workgroup
-constexpr int Q_TILE = 32;    // queries per tile
+constexpr int KV_BLK = 128;   // keys per dK/dV workgroup
+constexpr int Q_TILE = 32;    // queries per dK/dV tile
+constexpr int Q_BLK = 128;    // queries per dQ workgroup
+constexpr int K_TILE = 64;    // keys per dQ tile
 
 template <int D>
 struct DkdvLds {
@@ -145,24 +147,43 @@ struct DkdvLds {
   static constexpr int ELEMS = V_ELEMS + 2 * STAGE;
 };
 
+template <int D>
+struct DqLds {
+  static constexpr int KS = both_ways_stride<D>();   // K tile: row reads and transpose reads
+  static constexpr int VS = row_read_stride<D>();    // V tile: row reads
+  static constexpr int K_ELEMS = K_TILE * KS;
+  static constexpr int STAGE = K_ELEMS + K_TILE * VS;
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
+// One LDS buffer, big enough for either kernel's tiles, used by every
+// backward kernel of one head dimension.
+template <int D>
+__device__ __forceinline__ uint16_t* bwd_lds() {
+  constexpr int E = DkdvLds<D>::ELEMS > DqLds<D>::ELEMS ? DkdvLds<D>::ELEMS : DqLds<D>::ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t buf[E];
+  return buf;
+}
+
+// One workgroup's work for block id `wid` of a grid of `total` blocks.
 // WRITE_DS: also store dS (bf16, row stride Nk) for the stored-dS dQ.
 template <int D, bool CAUSAL, bool WRITE_DS>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
-bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                const uint16_t* __restrict__ V, const float* __restrict__ LSE,
-                const uint16_t* __restrict__ dO, const float* __restrict__ delta,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkb, int total,
-                float c, float scale, uint16_t* __restrict__ dS, int Nk) {
+__device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__ Q,
+                                           const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                           const float* __restrict__ LSE, const uint16_t* __restrict__ dO,
+                                           const float* __restrict__ delta, uint16_t* __restrict__ dK,
+                                           uint16_t* __restrict__ dV, int N, int nkb, int total, float c,
+                                           float scale, uint16_t* __restrict__ dS, int Nk) {
   using L = DkdvLds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  uint16_t* smem = bwd_lds<D>();
   uint16_t* Vs = smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, g = lane >> 5;
   int bh, kb;
-  map_block(blockIdx.x, total, nkb, CAUSAL ? 2 : 0, bh, kb);  // causal: low key blocks carry the most work
+  map_block(wid, total, nkb, CAUSAL ? 2 : 0, bh, kb);  // causal: low key blocks carry the most work
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
@@ -330,34 +351,33 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-// ---------------------------------------------------------------- dQ
-constexpr int Q_BLK = 128;    // queries per workgroup
-constexpr int K_TILE = 64;    // keys per tile
-
-template <int D>
-struct DqLds {
-  static constexpr int KS = both_ways_stride<D>();   // K tile: row reads and transpose reads
-  static constexpr int VS = row_read_stride<D>();    // V tile: row reads
-  static constexpr int K_ELEMS = K_TILE * KS;
-  static constexpr int STAGE = K_ELEMS + K_TILE * VS;
-  static constexpr int ELEMS = 2 * STAGE;
-};
-
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WRITE_DS>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
-bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, const float* __restrict__ LSE,
-              const uint16_t* __restrict__ dO, const float* __restrict__ delta,
-              uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
+bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                const uint16_t* __restrict__ V, const float* __restrict__ LSE,
+                const uint16_t* __restrict__ dO, const float* __restrict__ delta,
+                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nkb, int total,
+                float c, float scale, uint16_t* __restrict__ dS, int Nk) {
+  dkdv_block<D, CAUSAL, WRITE_DS>(blockIdx.x, Q, K, V, LSE, dO, delta, dK, dV, N, nkb, total, c, scale, dS,
+                                  Nk);
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q,
+                                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                         const float* __restrict__ LSE, const uint16_t* __restrict__ dO,
+                                         const float* __restrict__ delta, uint16_t* __restrict__ dQ, int N,
+                                         int nqb, int total, float c, float scale) {
   using L = DqLds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
+  uint16_t* smem = bwd_lds<D>();
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, g = lane >> 5;
   int bh, qb;
-  map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
+  map_block_xcd(wid, total, nqb, CAUSAL, bh, qb);
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
@@ -444,6 +464,36 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   for (; j < ntiles; ++j) step(j, std::true_type{});
 
   if (myq < N) store_acc_row<D>(dQ + base + (size_t)myq * D, dqt, scale, g);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
+bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, const float* __restrict__ LSE,
+              const uint16_t* __restrict__ dO, const float* __restrict__ delta,
+              uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
+  dq_block<D, CAUSAL>(blockIdx.x, Q, K, V, LSE, dO, delta, dQ, N, nqb, total, c, scale);
+}
+
+// dK/dV and dQ in one launch: ids 16j .. 16j+7 run dK/dV block 8j + (id % 8)
+// and ids 16j+8 .. 16j+15 dQ block 8j + (id % 8), so both kinds of work sit
+// on every XCD (id % 8) in the order each grid would dispatch them, and the
+// dQ blocks fill in behind the dK/dV blocks' tail and the reverse.  The two
+// grids have the same number of blocks (128 keys or 128 queries each).
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
+bwd_fused_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                 const uint16_t* __restrict__ V, const float* __restrict__ LSE,
+                 const uint16_t* __restrict__ dO, const float* __restrict__ delta,
+                 uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int nb,
+                 int total, float c, float scale) {
+  const int w = blockIdx.x;
+  const int vid = 8 * (w >> 4) + (w & 7);
+  if (vid >= total) return;
+  if ((w & 8) == 0)
+    dkdv_block<D, CAUSAL, false>(vid, Q, K, V, LSE, dO, delta, dK, dV, N, nb, total, c, scale, nullptr, 0);
+  else
+    dq_block<D, CAUSAL>(vid, Q, K, V, LSE, dO, delta, dQ, N, nb, total, c, scale);
 }
 
 // ---------------------------------------------------------------- dQ from stored dS
@@ -556,6 +606,20 @@ hipError_t launch_stored_ds(const uint16_t* q, const uint16_t* k, const uint16_t
 }
 
 template <int D, bool CAUSAL>
+hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                        const uint16_t* dO, const float* delta, uint16_t* dq, uint16_t* dk, uint16_t* dv, int BH,
+                        int N, float scale, hipStream_t stream) {
+  static_assert(KV_BLK == Q_BLK, "the fused grid pairs key blocks with query blocks");
+  const int nb = (N + KV_BLK - 1) / KV_BLK;
+  const long long total = (long long)BH * nb;
+  const long long grid = 16 * ((total + 7) / 8);
+  if (grid > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(NT), 0, stream, q, k, v, lse, dO,
+                     delta, dq, dk, dv, N, nb, (int)total, score_coef(scale), scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 hipError_t launch_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
                      const uint16_t* dO, const float* delta, uint16_t* dq, int BH, int N, float scale,
                      hipStream_t stream) {
@@ -616,6 +680,16 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float scale, float* delta, hipStream_t stream) {
   hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
   if (e != hipSuccess) return e;
+  // While each kernel's grid fits on the chip at once (256 CUs x the waves
+  // per SIMD), the two run better side by side in one launch than one after
+  // the other; beyond that the separate launches are faster.
+  const long long blocks = (long long)BH * ((N + KV_BLK - 1) / KV_BLK);
+  if (d == 64 && blocks <= 256 * bwd_waves_per_simd<64>())
+    return causal ? launch_fused<64, true>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream)
+                  : launch_fused<64, false>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
+  if (d == 128 && blocks <= 256 * bwd_waves_per_simd<128>())
+    return causal ? launch_fused<128, true>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream)
+                  : launch_fused<128, false>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
   e = launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, BH, N, d, causal, scale, stream);
   if (e != hipSuccess) return e;
   return launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, BH, N, d, causal, scale, stream);

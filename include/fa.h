@@ -217,7 +217,10 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  * fa_backward_preprocess, then fa_backward_dkdv and fa_backward_dq (in either
  * order) on one stream with the same workspace gives exactly what
  * fa_backward gives; they exist so that callers can time or schedule the
- * stages one by one.  Arguments mean what they mean for fa_backward.
+ * stages one by one.  (fa_backward itself runs the dK/dV and dQ work in one
+ * launch when each of the two grids fits on the device at once, so that the
+ * two kinds of workgroup share the compute units; the arithmetic per output
+ * is the same either way.)  Arguments mean what they mean for fa_backward.
  *   fa_backward_preprocess: workspace rows delta_i = sum_c dO_ic * O_ic.
  *   fa_backward_dkdv: dK and dV, one workgroup per 128 keys, looping over
  *     query tiles (reads q, k, v, lse, dO and the workspace).

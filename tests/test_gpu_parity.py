@@ -264,6 +264,47 @@ def test_full_size_backward(fa):
             assert e <= TOL_BF16, f"{name} head {(b, h)}: {e:.4g} (storage floor {storage_floor(r):.3g})"
 
 
+
+# (B, H, N, d, causal): up to 512 workgroups per grid at d=128 (768 at d=64)
+# fa_backward runs dK/dV and dQ in one launch, above that in two.
+STAGE_SHAPES = [(1, 16, 2048, 128, True), (2, 16, 2048, 128, True), (2, 16, 2048, 128, False),
+                (4, 16, 2048, 128, True), (3, 5, 1000, 128, True), (1, 1, 1, 128, False),
+                (6, 16, 1024, 64, True), (7, 16, 1024, 64, False), (4, 16, 2048, 64, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", STAGE_SHAPES)
+def test_backward_equals_its_stages(fa, B, H, N, d, causal):
+    """fa_backward (one launch for both passes on small grids, two on large
+    ones) gives the same bits as fa_backward_preprocess, fa_backward_dkdv and
+    fa_backward_dq called one by one; sampled heads agree with the oracle."""
+    import torch
+
+    q, k, v, do = random_inputs(500 + N + B, (B, H, N, d), "bf16", 4)
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(tq, tk, tv, causal=causal, scale=scale)
+    whole = fa.backward(tq, tk, tv, o, lse, tdo, causal=causal, scale=scale)
+    staged = [torch.full_like(tq, float("nan")) for _ in range(3)]
+    nb = fa.fa_backward_workspace_size(B, H, N, d)
+    ws = torch.empty(nb, dtype=torch.uint8, device=tq.device)
+    sp = torch.cuda.current_stream().cuda_stream
+    assert fa.fa_backward_preprocess(o.data_ptr(), tdo.data_ptr(), B, H, N, d, ws.data_ptr(), nb, sp) == 0
+    assert fa.fa_backward_dq(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), lse.data_ptr(), tdo.data_ptr(),
+                             staged[0].data_ptr(), B, H, N, d, causal, scale, ws.data_ptr(), nb, sp) == 0
+    assert fa.fa_backward_dkdv(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), lse.data_ptr(), tdo.data_ptr(),
+                               staged[1].data_ptr(), staged[2].data_ptr(), B, H, N, d, causal, scale,
+                               ws.data_ptr(), nb, sp) == 0
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), whole, staged):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    got = [host64(t) for t in whole]
+    for (b, h) in sorted({(0, 0), (B - 1, H - 1)}):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = oracle.attention_backward(*(fi.exact_f64(a[sl]) for a in (q, k, v, do)), causal, scale)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            e = max_abs(g[sl], r)
+            assert e <= TOL_BF16, f"{name} head {(b, h)}: {e:.4g} (storage floor {storage_floor(r):.3g})"
+
 def test_forward_is_deterministic_across_streams(fa):
     import torch
 
