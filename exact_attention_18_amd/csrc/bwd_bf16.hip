@@ -18,7 +18,9 @@
 // the orientation (S or S^T) in which its register-resident rows sit on the
 // lanes.  Tiles stay row-major in LDS; operands that need the other
 // orientation come from the LDS transpose read.  Tiles are double-buffered:
-// tile i+1 is fetched into registers while tile i is computed.
+// tile i+1 is fetched while tile i is computed (the dK/dV kernel's Q and dO
+// tiles by direct HBM-to-LDS loads, the dQ kernel's K and V tiles through
+// registers).
 //
 // Stored-dS variant (a caller workspace of B*H*N*Nk bf16, Nk = N rounded up
 // to 128): the dK/dV kernel also writes dS, row q holding dS[q][k] for every
@@ -30,8 +32,9 @@
 // of dS is the B operand matching a transpose-read K operand.
 //
 // Ragged N needs no masks here: rows past N read as zero (buffer loads), a
-// zero key row contributes nothing to dQ, a query past N has LSE = +inf so
-// its P is 0, and results for keys or queries past N are never stored.
+// zero key row contributes nothing to dQ, a query past N has a zero dO row
+// and delta (so dS = 0 and P^T dO = 0 whatever its P), and results for keys
+// or queries past N are never stored.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -81,6 +84,20 @@ struct Rows {
     }
   }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct HBM -> LDS load: lane l's 16 bytes at byte `off` of the buffer land
+// at dst + 16 l (dst wave-uniform); an offset past the buffer writes zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, off, 0, 0, 0);
+}
+// Wait until this wave's direct LDS loads (and all its other vector memory
+// operations) are complete.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Row `row` of a row-major tile, 16-byte block ks*16 + 8*g: a 32x32x16
 // operand whose rows sit on the lanes.
@@ -140,9 +157,16 @@ template <int D>
 struct DkdvLds {
   static constexpr int QS = both_ways_stride<D>();   // Q and dO tiles
   static constexpr int VS = row_read_stride<D>();    // the workgroup's V rows
-  static constexpr int TILE = Q_TILE * QS;
-  // one stage: Q tile, dO tile, then LSE*log2(e) and delta (2 x 32 floats)
-  static constexpr int STAGE = 2 * TILE + 2 * Q_TILE * 2;
+  // The Q and dO tiles are filled by direct loads of 64 x 16 bytes (one per
+  // lane, in order), so each tile's region is a whole number of such blocks:
+  // RI loads cover the Q_TILE padded rows, the rest of the last block is a
+  // zero-filled gap.
+  static constexpr int CPRP = QS / 8;                          // 16-byte chunks per padded row
+  static constexpr int RI = (Q_TILE * CPRP + 63) / 64;         // loads per tile
+  static constexpr int TILE = RI * 512;                        // region, elements
+  // one stage: Q region, dO region, then LSE and delta (2 x 64 floats, the
+  // first 32 of each used)
+  static constexpr int STAGE = 2 * TILE + 2 * 64 * 2;
   static constexpr int V_ELEMS = KV_BLK * VS;
   static constexpr int ELEMS = V_ELEMS + 2 * STAGE;
 };
@@ -223,29 +247,35 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   const int qstart = CAUSAL ? k0 : 0;
   const int ntiles = (N - qstart + Q_TILE - 1) / Q_TILE;
 
-  // Per-tile staging: Q and dO rows, and LSE*log2(e) and delta of the tile's
-  // queries (queries past N get LSE = +inf, so their P is 0).
-  Rows<Q_TILE, D> qrows, grows;
-  uint32_t lse_bits = 0, dl_bits = 0;
-  const int qsel = tid & (Q_TILE - 1);
-  auto fetch = [&](int qt0) {
-    qrows.load(qrs, qt0, tid);
-    grows.load(grs, qt0, tid);
-    lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + qsel) * 4, 0, 0);
-    dl_bits = __builtin_amdgcn_raw_buffer_load_b32(drs, (uint32_t)(qt0 + qsel) * 4, 0, 0);
-  };
-  auto put = [&](int qt0, uint16_t* stage) {
-    qrows.template store<L::QS>(stage, tid);
-    grows.template store<L::QS>(stage + L::TILE, tid);
-    if (tid < Q_TILE) {
-      float* f = reinterpret_cast<float*>(stage + 2 * L::TILE);
-      f[tid] = qt0 + tid < N ? __uint_as_float(lse_bits) * kLog2e : INFINITY;
-      f[Q_TILE + tid] = __uint_as_float(dl_bits);
+  // Per-tile loads, straight into LDS: the Q and dO rows, the LSE and delta
+  // of the tile's queries.  Queries past N read as zero throughout, which
+  // makes their P = exp2(0) = 1 but their dO row, dP and delta zero, so they
+  // add nothing to dV (P^T dO) or dK (dS^T Q with dS = P (dP - delta) = 0).
+  // Load j of the 2 RI per tile (Q then dO) is issued by wave j % 4; lane l
+  // of load jj of a matrix fills 16-byte chunk 64 jj + l of its region.
+  constexpr int NJ = (2 * L::RI + 3) / 4;   // loads per wave, at most
+  uint32_t voff[NJ];
+#pragma unroll
+  for (int u = 0; u < NJ; ++u) {
+    const int jj = (wave + 4 * u) % L::RI;
+    const int p = 64 * jj + lane, row = p / L::CPRP, col = p % L::CPRP;
+    voff[u] = row < Q_TILE && col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
+  }
+  auto fetch = [&](int qt0, uint16_t* stage) {
+#pragma unroll
+    for (int u = 0; u < NJ; ++u) {
+      const int j = wave + 4 * u;
+      if (j < 2 * L::RI) {
+        const int m = j / L::RI, jj = j % L::RI;
+        lds_load16(m ? grs : qrs, stage + m * L::TILE + jj * 512, voff[u] + (uint32_t)qt0 * D * 2);
+      }
     }
+    if (wave == 2) lds_load4(lrs, stage + 2 * L::TILE, (uint32_t)(qt0 + lane) * 4);
+    if (wave == 3) lds_load4(drs, stage + 2 * L::TILE + 128, (uint32_t)(qt0 + lane) * 4);
   };
 
-  fetch(qstart);
-  put(qstart, smem + L::V_ELEMS);
+  fetch(qstart, smem + L::V_ELEMS);
+  wait_vmem();
   __syncthreads();
 
   // One query tile for this wave.  MASK: the tile may straddle the diagonal
@@ -255,9 +285,9 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     const int qt0 = qstart + i * Q_TILE;
     const uint16_t* Qs = smem + L::V_ELEMS + (i & 1) * L::STAGE;
     const uint16_t* Gs = Qs + L::TILE;
-    const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * L::TILE);
-    const float* dls = lse2 + Q_TILE;
-    if (i + 1 < ntiles) fetch(qt0 + Q_TILE);
+    const float* lse = reinterpret_cast<const float*>(Qs + 2 * L::TILE);
+    const float* dls = lse + 64;
+    if (i + 1 < ntiles) fetch(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
 
     if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
       // S and dP: element r is query qt0 + 8(r/4) + 4g + r%4, key myk.
@@ -285,12 +315,12 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       const int lim = myk - qt0 - 4 * g;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * a + 4 * g);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + 8 * a + 4 * g);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
-          float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b]));
+          float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b] * kLog2e));
           if (CAUSAL && MASK && 8 * a + b < lim) p = 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - d4[b]);
@@ -335,7 +365,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       for (int r = 0; r < 16; ++r)
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)0, dsr, ds_off, ds_row(qt0, r), 0);
     }
-    if (i + 1 < ntiles) put(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
+    wait_vmem();
     __syncthreads();
   };
   // Causal: the first KV_BLK / Q_TILE tiles straddle the diagonals of the
