@@ -18,9 +18,8 @@
 // the orientation (S or S^T) in which its register-resident rows sit on the
 // lanes.  Tiles stay row-major in LDS; operands that need the other
 // orientation come from the LDS transpose read.  Tiles are double-buffered:
-// tile i+1 is fetched while tile i is computed (the dK/dV kernel's Q and dO
-// tiles by direct HBM-to-LDS loads, the dQ kernel's K and V tiles through
-// registers).
+// tile i+1 is fetched by direct HBM-to-LDS loads while tile i is computed
+// (the stored-dS dQ kernel stages its K tiles through registers).
 //
 // Stored-dS variant (a caller workspace of B*H*N*Nk bf16, Nk = N rounded up
 // to 128): the dK/dV kernel also writes dS, row q holding dS[q][k] for every
@@ -178,6 +177,10 @@ struct DqLds {
   static constexpr int K_ELEMS = K_TILE * KS;
   static constexpr int STAGE = K_ELEMS + K_TILE * VS;
   static constexpr int ELEMS = 2 * STAGE;
+  // direct loads of 64 x 16 bytes fill each tile's padded rows in order
+  static constexpr int KCPR = KS / 8, VCPR = VS / 8;
+  static constexpr int KLOADS = K_TILE * KCPR / 64, VLOADS = K_TILE * VCPR / 64;
+  static_assert(KLOADS * 64 == K_TILE * KCPR && VLOADS * 64 == K_TILE * VCPR, "tiles must be whole loads");
 };
 
 // One LDS buffer, big enough for either kernel's tiles, used by every
@@ -436,11 +439,32 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
 
   const int kv_end = CAUSAL ? min(N, q0 + Q_BLK) : N;
   const int ntiles = (kv_end + K_TILE - 1) / K_TILE;
-  Rows<K_TILE, D> krows, vrows;
-  krows.load(krs, 0, tid);
-  vrows.load(vrs, 0, tid);
-  krows.template store<L::KS>(smem, tid);
-  vrows.template store<L::VS>(smem + L::K_ELEMS, tid);
+  // K and V tiles come by direct HBM -> LDS loads: load j of a tile pair (K
+  // loads first, then V) is issued by wave j % 4, and lane l of a load fills
+  // the 16-byte chunk 64 (its index within the tile) + l of the padded rows;
+  // lanes on a row's padding get an offset past the buffer (zeros).
+  constexpr int NL = L::KLOADS + L::VLOADS, PW = (NL + 3) / 4;
+  uint32_t voff[PW];
+#pragma unroll
+  for (int u = 0; u < PW; ++u) {
+    const int j = wave + 4 * u;
+    const bool isv = j >= L::KLOADS;
+    const int cpr = isv ? L::VCPR : L::KCPR;
+    const int p = 64 * (isv ? j - L::KLOADS : j) + lane, row = p / cpr, col = p % cpr;
+    voff[u] = col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
+  }
+  auto fetch = [&](int kv0, uint16_t* stage) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + 4 * u;
+      if (j < L::KLOADS)
+        lds_load16(krs, stage + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
+      else if (j < NL)
+        lds_load16(vrs, stage + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
+    }
+  };
+  fetch(0, smem);
+  wait_vmem();
   __syncthreads();
 
   auto step = [&](int j, auto mask_tag) {
@@ -448,10 +472,7 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
     const int kv0 = j * K_TILE;
     const uint16_t* Ks = smem + (j & 1) * L::STAGE;
     const uint16_t* Vs = Ks + L::K_ELEMS;
-    if (j + 1 < ntiles) {
-      krows.load(krs, kv0 + K_TILE, tid);
-      vrows.load(vrs, kv0 + K_TILE, tid);
-    }
+    if (j + 1 < ntiles) fetch(kv0 + K_TILE, smem + ((j + 1) & 1) * L::STAGE);
     if (!CAUSAL || !MASK || kv0 <= qw + 31) {
       // hidden when key > myq, i.e. key offset 32kb + 8(r/4) + r%4 > lim
       const int lim = myq - kv0 - 4 * g;
@@ -479,11 +500,7 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
         }
       }
     }
-    if (j + 1 < ntiles) {
-      uint16_t* nxt = smem + ((j + 1) & 1) * L::STAGE;
-      krows.template store<L::KS>(nxt, tid);
-      vrows.template store<L::VS>(nxt + L::K_ELEMS, tid);
-    }
+    wait_vmem();
     __syncthreads();
   };
   // Tiles below every query's diagonal run unmasked; the last (at most two)
