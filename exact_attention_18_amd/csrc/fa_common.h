@@ -142,4 +142,19 @@ __device__ __forceinline__ void map_block_xcd(int w, int total, int nq, bool hea
   map_block(w, total, nq, heavy_first ? 1 : 0, bh, qb);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct HBM -> LDS load: lane l's 16 (or 4) bytes at byte `off` of the
+// buffer land at dst + 16 l (4 l), dst wave-uniform; an offset past the
+// buffer writes zeros.  Checked on the device: lane order, zero fill.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, off, 0, 0, 0);
+}
+// Wait until this wave's direct LDS loads (and all its other vector memory
+// operations) are complete.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace fa

@@ -8,7 +8,8 @@
 //    32 queries and share every K/V tile (the query split across warps of
 //    FlashAttention-2, on 64-wide waves);
 //  * K/V tiles of 64 keys stream through a double-buffered LDS stage; tile j+1
-//    is fetched into registers while tile j is computed;
+//    is fetched by direct HBM-to-LDS loads while tile j is computed (the
+//    two-group kernel below stages its tiles through registers);
 //  * S^T = K Q^T and O^T += V^T P^T on the bf16 matrix cores.  Computing the
 //    transposed products puts one query per lane (two lanes per query), so
 //    the row max, the row sum and the output rescale are per-lane values.
@@ -54,41 +55,45 @@ struct Lds {
   static constexpr int K_ELEMS = BC * KS;
   static constexpr int STAGE = K_ELEMS + BC * VS;
   static constexpr int ELEMS = 2 * STAGE;              // double buffer
-  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / NT;            // chunks per thread per tensor
+  // direct loads of 64 x 16 bytes fill a tile's padded rows in order
+  static constexpr int KCPR = KS / 8, VCPR = VS / 8;   // chunks per padded row
+  static constexpr int KLOADS = BC * KCPR / 64, VLOADS = BC * VCPR / 64;
+  static_assert(KLOADS * 64 == BC * KCPR && VLOADS * 64 == BC * VCPR, "tiles must be whole loads");
 };
 
-template <int D>
-struct TileRegs {
-  u32x4 k[Lds<D>::CPT];
-  u32x4 v[Lds<D>::CPT];
-};
-
-// Global -> registers for the tile starting at key kv0.  Buffer loads: rows
-// at or beyond N lie past the end of the buffer and read as zero.
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                          int kv0, int tid) {
-#pragma unroll
-  for (int i = 0; i < Lds<D>::CPT; ++i) {
-    const int c = tid + NT * i;
-    const uint32_t off = (uint32_t)(((kv0 + c / Lds<D>::CPR) * D + (c % Lds<D>::CPR) * 8) * 2);
-    r.k[i] = buf_load16(kr, off);
-    r.v[i] = buf_load16(vr, off);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, uint16_t* stage, int tid) {
+// A K tile and a V tile of 64 rows by direct HBM -> LDS loads, shared out
+// over NW waves: load j (K loads first, then V) is issued by wave j % NW, and
+// lane l of a load fills 16-byte chunk 64 (its index within the tile) + l of
+// the tile's padded rows.  Lanes on a row's padding get an offset past the
+// buffer (zeros); rows at or past N read as zero as well.
+template <int D, int NW>
+struct TileDma {
   using L = Lds<D>;
+  static constexpr int NL = L::KLOADS + L::VLOADS, PW = (NL + NW - 1) / NW;
+  uint32_t voff[PW];
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < L::CPT; ++i) {
-    const int c = tid + NT * i;
-    const int row = c / L::CPR, col = (c % L::CPR) * 8;
-    *reinterpret_cast<u32x4*>(stage + row * L::KS + col) = r.k[i];
-    *reinterpret_cast<u32x4*>(stage + L::K_ELEMS + row * L::VS + col) = r.v[i];
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + NW * u;
+      const bool isv = j >= L::KLOADS;
+      const int cpr = isv ? L::VCPR : L::KCPR;
+      const int p = 64 * (isv ? j - L::KLOADS : j) + lane, row = p / cpr, col = p % cpr;
+      voff[u] = col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
+    }
   }
-}
+  // Tile starting at key kv0 into the stage at dst (K, then V at K_ELEMS).
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kv0,
+                                        uint16_t* dst, int wave) const {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + NW * u;
+      if (j < L::KLOADS)
+        lds_load16(kr, dst + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
+      else if (j < NL)
+        lds_load16(vr, dst + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
+    }
+  }
+};
 
 // Online-softmax bookkeeping for one wave's 64-key tile of S^T (element r of
 // s[kb] is key 32*kb + 8*(r/4) + 4*g + r%4): optional mask (keys past `lim`
@@ -250,7 +255,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m = -INFINITY;   // reference max of scale*log2e*s for query myq
   float lsum = 0.f;      // this lane's share of the row sum
 
-  TileRegs<D> regs;
+  TileDma<D, NT / 64> dma;
+  dma.init(wave, lane);
   if constexpr (SPARSE) {
     // Visit only the tiles of visible key blocks and prefetch the next
     // visible one.  A key block is two 64-key tiles.  The mask row is read
@@ -275,10 +281,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       return nqb;
     };
     int j = 2 * first_visible_block(0);
-    if (j < ntiles) {
-      load_tile<D>(regs, krs, vrs, j * BC, tid);
-      store_tile<D>(regs, smem, tid);
-    }
+    if (j < ntiles) dma.issue(krs, vrs, j * BC, smem, wave);
+    wait_vmem();
     __syncthreads();
     int slot = 0;
     while (j < ntiles) {
@@ -286,19 +290,19 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const uint16_t* Ks = smem + slot * L::STAGE;
       const uint16_t* Vs = Ks + L::K_ELEMS;
       const int kv0 = j * BC;
-      if (jn < ntiles) load_tile<D>(regs, krs, vrs, jn * BC, tid);
+      if (jn < ntiles) dma.issue(krs, vrs, jn * BC, smem + (slot ^ 1) * L::STAGE, wave);
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
         tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
       }
-      if (jn < ntiles) store_tile<D>(regs, smem + (slot ^ 1) * L::STAGE, tid);
+      wait_vmem();
       __syncthreads();
       slot ^= 1;
       j = jn;
     }
   } else {
-  load_tile<D>(regs, krs, vrs, 0, tid);
-  store_tile<D>(regs, smem, tid);
+  dma.issue(krs, vrs, 0, smem, wave);
+  wait_vmem();
   __syncthreads();
 
   // Interior tiles (no key of the tile is hidden from any query of the
@@ -311,7 +315,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* Ks = smem + (j & 1) * L::STAGE;
     const uint16_t* Vs = Ks + L::K_ELEMS;
     const int kv0 = j * BC;
-    if (j + 1 < ntiles) load_tile<D>(regs, krs, vrs, kv0 + BC, tid);
+    if (j + 1 < ntiles) dma.issue(krs, vrs, kv0 + BC, smem + ((j + 1) & 1) * L::STAGE, wave);
     if constexpr (MASK) {
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
@@ -320,7 +324,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     } else {
       tile_step<D, false>(Ks, Vs, qf, oacc, m, lsum, c, 0, lane);
     }
-    if (j + 1 < ntiles) store_tile<D>(regs, smem + ((j + 1) & 1) * L::STAGE, tid);
+    wait_vmem();
     __syncthreads();
   };
   int j = 0;
@@ -843,11 +847,10 @@ fwd_sparse_balanced_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     int blk = o1 > o0 ? nth_visible(o0) : kend;
     int blocks_left = o1 - o0;                        // blocks of this item not yet finished
     int j = blk < kend ? 2 * blk : ntiles;
-    TileRegs<D> regs;
-    if (j < ntiles) {
-      load_tile<D>(regs, krs, vrs, j * BC, tid);
-      store_tile<D>(regs, smem, tid);
-    }
+    TileDma<D, NT / 64> dma;
+    dma.init(wave, lane);
+    if (j < ntiles) dma.issue(krs, vrs, j * BC, smem, wave);
+    wait_vmem();
     __syncthreads();
     int slot = 0;
     while (j < ntiles) {
@@ -862,12 +865,12 @@ fwd_sparse_balanced_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
       const uint16_t* Ks = smem + slot * L::STAGE;
       const uint16_t* Vs = Ks + L::K_ELEMS;
       const int kv0 = j * BC;
-      if (jn < ntiles) load_tile<D>(regs, krs, vrs, jn * BC, tid);
+      if (jn < ntiles) dma.issue(krs, vrs, jn * BC, smem + (slot ^ 1) * L::STAGE, wave);
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
         tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
       }
-      if (jn < ntiles) store_tile<D>(regs, smem + (slot ^ 1) * L::STAGE, tid);
+      wait_vmem();
       __syncthreads();
       slot ^= 1;
       j = jn;
