@@ -17,9 +17,11 @@
 //    transpose read;
 //  * online softmax in the base-2 domain: scale*log2(e) is folded into one
 //    multiply-add before v_exp_f32; the running max is only raised when a
-//    tile's max exceeds it by more than 2^8 (the numerator and denominator
-//    share the reference, so the result is unchanged); 1/l is applied once,
-//    in the epilogue;
+//    tile's max exceeds it by more than 8 (log2 units; the numerator and
+//    denominator share the reference, so the result is unchanged), which the
+//    tile's exponentials themselves reveal (some p > 2^8), so the row max is
+//    only computed in the rare tiles that need it; 1/l is applied once, in
+//    the epilogue;
 //  * causal: tiles above the diagonal are never loaded; the mask code runs
 //    only on tiles that straddle the diagonal or the ragged end of N.
 #include <type_traits>
@@ -34,6 +36,7 @@ constexpr int BR = 128;       // queries per workgroup
 constexpr int BC = 64;        // keys per tile
 constexpr int NT = 256;       // threads per workgroup (4 waves)
 constexpr float TAU = 8.0f;   // lazy-rescale threshold, log2 units
+constexpr float PMAX = 256.f;  // 2^TAU
 
 // Row padding (elements) of the K and V tiles in LDS; tuning knobs.
 #ifndef FA_FWD_KPAD
@@ -137,6 +140,55 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D 
   }
 }
 
+// P = exp2(c s - m) for one wave's 64-key tile, packed to bf16 into pw
+// (block b = 2 kb + t holds keys 32 kb + 16 t + ...), added to the row sum,
+// with the lazy rescale of m.  Fast path: P with the current reference max.
+// It stands when no p exceeds 2^TAU, which each block sum (at least its
+// largest p) shows without a row max, and that is exactly when the lazy rule
+// keeps m.  Otherwise (also while m is still -inf, which gives inf or NaN)
+// the tile takes softmax_update and P is recomputed with the new m, as if
+// the fast path had not run.  Sums are added in the same order either way.
+template <int D, bool MASK>
+__device__ __forceinline__ void softmax_probs(f32x16 (&s)[2], u32x4 (&pw)[4], f32x16 (&oacc)[D / 32], float& m,
+                                              float& lsum, float c, int lim) {
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+  }
+  auto probs = [&](float& l) {
+    float bmax = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float ps[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * t + 2 * e;
+          const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
+          const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
+          ps[e] = p0 + p1;
+          pw[2 * kb + t][e] = pack_bf16x2(p0, p1);
+        }
+        const float bs = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        l += bs;
+        bmax = max_nan(bmax, bs);
+      }
+    return bmax;
+  };
+  float l = lsum;
+  const float bmax = probs(l);
+  if (__any(!(bmax <= PMAX))) {
+    softmax_update<D, false>(s, oacc, m, lsum, c, 0);
+    l = lsum;
+    probs(l);
+  }
+  lsum = l;
+}
+
 // One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax update,
 // O^T += V^T P^T.  MASK selects the variant for tiles that straddle the
 // diagonal or the end of N; `lim` is the largest visible key offset within
@@ -172,28 +224,16 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 
-  softmax_update<D, MASK>(s, oacc, m, lsum, c, lim);
+  u32x4 pw[4];
+  softmax_probs<D, MASK>(s, pw, oacc, m, lsum, c, lim);
 
-  // Exponentials of block (kb, t) then its four PV products, so the matrix
-  // cores can run block b while the VALU computes block b+1.
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      u32x4 w;
-      float ps[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * t + 2 * e;
-        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
-        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
-        ps[e] = p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
-      }
-      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, w);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[2 * kb + t]);
       const uint16_t* vp = Vs + (kb * 32 + 16 * t + tr_row) * L::VS + tr_col;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -464,28 +504,12 @@ __device__ __forceinline__ void pp_matrix(const uint16_t* Ks, const uint16_t* Vs
   }
 }
 
-// Softmax phase: softmax_update on S, then P = exp2(c s - m) packed to bf16
-// into pw (block b = (kb, t) holds keys 32 kb + 16 t + ...), row sum into
-// lsum, in the order tile_step uses.
+// Softmax phase: softmax_probs on S (P packed to bf16 into pw, row sum into
+// lsum), exactly as tile_step does it.
 template <int D, bool MASK>
 __device__ __forceinline__ void pp_softmax(f32x16 (&s)[2], u32x4 (&pw)[4], f32x16 (&oacc)[D / 32], float& m,
                                            float& lsum, float c, int lim) {
-  softmax_update<D, MASK>(s, oacc, m, lsum, c, lim);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float ps[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * t + 2 * e;
-        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
-        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
-        ps[e] = p0 + p1;
-        pw[2 * kb + t][e] = pack_bf16x2(p0, p1);
-      }
-      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
+  softmax_probs<D, MASK>(s, pw, oacc, m, lsum, c, lim);
 }
 
 // Workgroup barrier that is also a scheduling fence.

@@ -320,6 +320,28 @@ def test_forward_is_deterministic_across_streams(fa):
         assert torch.equal(lse, rl)
 
 
+
+@pytest.mark.parametrize("N,d,causal", [(2048, 128, False), (2048, 128, True), (3000, 128, True),
+                                        (2048, 64, False), (1500, 64, True)])
+def test_forward_scores_rising_along_keys(fa, N, d, causal):
+    """Scores that grow along the key axis (K_j = K0_j + t_j u, Q_i = Q0_i + u,
+    t_j from 0 to 6, |u|^2 = 100): every few tiles some score exceeds the
+    reference max by more than the lazy-rescale threshold, so the rescale
+    path runs repeatedly, in the middle of rows rather than only at their
+    first tile.  O and LSE against the oracle."""
+    rng = np.random.default_rng(1234 + N + d)
+    q0, k0, v = (rng.standard_normal((1, 2, N, d)).astype(np.float32) for _ in range(3))
+    u = rng.standard_normal(d).astype(np.float32)
+    u *= 10.0 / np.linalg.norm(u)
+    t = np.linspace(0.0, 6.0, N, dtype=np.float32)[None, None, :, None]
+    q, k, v = (fi.f32_to_bf16_bits(a) for a in (q0 + u, k0 + t * u, v))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run_fwd(fa, q, k, v, causal, scale)
+    ro, rl = oracle.attention_forward(fi.exact_f64(q), fi.exact_f64(k), fi.exact_f64(v), causal, scale)
+    eo, el = max_abs(host64(o), ro), max_abs(host64(lse), rl)
+    assert eo <= TOL_BF16, f"O error {eo:.3g} (storage floor {storage_floor(ro):.3g})"
+    assert el <= TOL_LSE, f"LSE error {el:.3g}"
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_magnitude_inputs(fa, causal):
     """Inputs x8 (scores up to ~1e3 * scale): the running max jumps by far
