@@ -266,42 +266,56 @@ __device__ __forceinline__ void fp8_tile_step(const uint8_t* st, const v8i* qf, 
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
   }
-  float m8[4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int r = 8 * hh;
-      const float a = max_nan(max_nan(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
-      const float b = max_nan(max_nan(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
-      m8[2 * kb + hh] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
-    }
-  float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
-  mx = max_halves(mx) * c;
-  if (__any(mx > m + FTAU)) {
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2_hw(m - mn);
-    m = mn;
-    lsum *= alpha;
-#pragma unroll
-    for (int i = 0; i < FD / 32; ++i) oacc[i] *= alpha;
-  }
-  // P^T operand: byte 16kb + r is p of accumulator element s[kb][r].
+  // P^T operand: byte 16kb + r is p of accumulator element s[kb][r].  The
+  // exponentials are first taken with the current reference max; only if
+  // some p exceeds 2^FTAU (its 4-element block sum shows it) or the
+  // reference is still -inf does the tile take the row max and the lazy
+  // rescale, and P is recomputed (the bf16 forward does the same).
   uint32_t pw[8];
-  float ps[8];
+  auto probs = [&](float& l) {
+    float ps[8];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int r = 4 * q4;
-      const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
-      const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
-      const float p2 = exp2_hw(__builtin_fmaf(s[kb][r + 2], c, -m));
-      const float p3 = exp2_hw(__builtin_fmaf(s[kb][r + 3], c, -m));
-      ps[4 * kb + q4] = (p0 + p1) + (p2 + p3);
-      pw[4 * kb + q4] = cvt_fp8x2(p2, p3, cvt_fp8x2(p0, p1, 0u, false), true);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r = 4 * q4;
+        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
+        const float p2 = exp2_hw(__builtin_fmaf(s[kb][r + 2], c, -m));
+        const float p3 = exp2_hw(__builtin_fmaf(s[kb][r + 3], c, -m));
+        ps[4 * kb + q4] = (p0 + p1) + (p2 + p3);
+        pw[4 * kb + q4] = cvt_fp8x2(p2, p3, cvt_fp8x2(p0, p1, 0u, false), true);
+      }
+    l += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    return max_nan(max_nan(max_nan(ps[0], ps[1]), max_nan(ps[2], ps[3])),
+                   max_nan(max_nan(ps[4], ps[5]), max_nan(ps[6], ps[7])));
+  };
+  float l = lsum;
+  if (__any(!(probs(l) <= 256.f))) {
+    float m8[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = 8 * hh;
+        const float a = max_nan(max_nan(s[kb][r], s[kb][r + 1]), s[kb][r + 2]);
+        const float b = max_nan(max_nan(s[kb][r + 3], s[kb][r + 4]), s[kb][r + 5]);
+        m8[2 * kb + hh] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
+      }
+    float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
+    mx = max_halves(mx) * c;
+    if (__any(mx > m + FTAU)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2_hw(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < FD / 32; ++i) oacc[i] *= alpha;
     }
-  lsum += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    l = lsum;
+    probs(l);
+  }
+  lsum = l;
   const v8i pb = v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
   const uint32_t vsc = Ve[h * 32 + l32];
   constexpr uint32_t ONE = 127u;
