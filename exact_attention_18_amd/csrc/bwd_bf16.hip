@@ -236,8 +236,9 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   const int qstart = CAUSAL ? k0 : 0;
   const int ntiles = (N - qstart + Q_TILE - 1) / Q_TILE;
 
-  // Per-tile loads, straight into LDS: the Q and dO rows, the LSE and delta
-  // of the tile's queries.  Queries past N read as zero throughout, which
+  // Per-tile loads, straight into LDS: the Q and dO rows and the delta of
+  // the tile's queries; wave 2 loads their LSE into a register and stores
+  // LSE * log2(e) at the end of the step.  Queries past N read as zero throughout, which
   // makes their P = exp2(0) = 1 but their dO row, dP and delta zero, so they
   // add nothing to dV (P^T dO) or dK (dS^T Q with dS = P (dP - delta) = 0).
   // Load j of the 2 RI per tile (Q then dO) is issued by wave j % 4; lane l
@@ -250,6 +251,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     const int p = 64 * jj + lane, row = p / L::CPRP, col = p % L::CPRP;
     voff[u] = row < Q_TILE && col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
   }
+  uint32_t lse_bits = 0;
   auto fetch = [&](int qt0, uint16_t* stage) {
 #pragma unroll
     for (int u = 0; u < NJ; ++u) {
@@ -259,11 +261,15 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         lds_load16(m ? grs : qrs, stage + m * L::TILE + jj * 512, voff[u] + (uint32_t)qt0 * D * 2);
       }
     }
-    if (wave == 2) lds_load4(lrs, stage + 2 * L::TILE, (uint32_t)(qt0 + lane) * 4);
+    if (wave == 2) lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + lane) * 4, 0, 0);
     if (wave == 3) lds_load4(drs, stage + 2 * L::TILE + 128, (uint32_t)(qt0 + lane) * 4);
+  };
+  auto put_lse = [&](uint16_t* stage) {
+    if (wave == 2) reinterpret_cast<float*>(stage + 2 * L::TILE)[lane] = __uint_as_float(lse_bits) * kLog2e;
   };
 
   fetch(qstart, smem + L::V_ELEMS);
+  put_lse(smem + L::V_ELEMS);
   wait_vmem();
   __syncthreads();
 
@@ -274,8 +280,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     const int qt0 = qstart + i * Q_TILE;
     const uint16_t* Qs = smem + L::V_ELEMS + (i & 1) * L::STAGE;
     const uint16_t* Gs = Qs + L::TILE;
-    const float* lse = reinterpret_cast<const float*>(Qs + 2 * L::TILE);
-    const float* dls = lse + 64;
+    const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * L::TILE);   // LSE * log2(e)
+    const float* dls = lse2 + 64;
     if (i + 1 < ntiles) fetch(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
 
     if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
@@ -304,12 +310,12 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       const int lim = myk - qt0 - 4 * g;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse + 8 * a + 4 * g);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * a + 4 * g);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
-          float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b] * kLog2e));
+          float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b]));
           if (CAUSAL && MASK && 8 * a + b < lim) p = 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - d4[b]);
@@ -354,6 +360,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       for (int r = 0; r < 16; ++r)
         __builtin_amdgcn_raw_buffer_store_b16((unsigned short)0, dsr, ds_off, ds_row(qt0, r), 0);
     }
+    if (i + 1 < ntiles) put_lse(smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
     wait_vmem();
     __syncthreads();
   };
