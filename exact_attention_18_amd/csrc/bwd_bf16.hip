@@ -7,7 +7,8 @@
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),
 //     dQ = scale * dS K,   dK = scale * dS^T Q.
 // Three launches on one stream, no atomics, so the result is bit-reproducible:
-//   1. delta (row-dot pre-pass, in f32_path.hip);
+//   1. -delta (row-dot pre-pass, in f32_path.hip; the negated sums let the
+//      dP accumulators start from them);
 //   2. dK/dV: one workgroup per (batch*head, 128 keys); each wave owns 32
 //      keys (K rows in registers) and loops over query tiles of 32 (causal:
 //      from the diagonal on);
@@ -285,13 +286,26 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     if (i + 1 < ntiles) fetch(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
 
     if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
-      // S and dP: element r is query qt0 + 8(r/4) + 4g + r%4, key myk.
-      f32x16 s, dp;
+      // S and dP: element r is query qt0 + 8(r/4) + 4g + r%4, key myk.  At
+      // d = 64 the dP accumulator starts from the tile's -delta values (the
+      // workspace holds -delta), which saves a subtraction per element; at
+      // d = 128 the extra live registers cost more than that saves, and the
+      // -delta is added after the product.
+      constexpr bool ND_INIT = D == 64;
+      f32x16 s, dp, nd = {};
+      if constexpr (ND_INIT) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) nd[4 * a + b] = d4[b];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         s = mfma32(row_operand<L::QS>(Qs, l32, ks, g), kf[ks], ks == 0 ? f32x16{} : s);
         dp = mfma32(row_operand<L::QS>(Gs, l32, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
-                    ks == 0 ? f32x16{} : dp);
+                    ks == 0 ? nd : dp);
       }
       // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
       // matrix-core instructions (mask 0x008), then 2 products per 3 reads
@@ -311,14 +325,15 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * a + 4 * g);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
+        f32x4 d4 = {};
+        if constexpr (!ND_INIT) d4 = *reinterpret_cast<const f32x4*>(dls + 8 * a + 4 * g);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
           float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b]));
           if (CAUSAL && MASK && 8 * a + b < lim) p = 0.f;
           s[r] = p;
-          dp[r] = p * (dp[r] - d4[b]);
+          dp[r] = ND_INIT ? p * dp[r] : p * (dp[r] + d4[b]);
         }
       }
 #pragma unroll
@@ -425,7 +440,12 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
     }
   }
   const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
-  const float dlv = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+  // -delta of this lane's query (the workspace holds -delta): the dP^T
+  // accumulators start from it
+  const float ndl = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+  f32x16 ndv;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndv[r] = ndl;
   f32x16 dqt[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqt[i] = f32x16{};
@@ -476,13 +496,13 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           s = mfma32(row_operand<L::KS>(Ks, kb * 32 + l32, ks, g), qf[ks], ks == 0 ? f32x16{} : s);
-          dp = mfma32(row_operand<L::VS>(Vs, kb * 32 + l32, ks, g), gf[ks], ks == 0 ? f32x16{} : dp);
+          dp = mfma32(row_operand<L::VS>(Vs, kb * 32 + l32, ks, g), gf[ks], ks == 0 ? ndv : dp);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
           if (CAUSAL && MASK && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
-          dp[r] = p * (dp[r] - dlv);
+          dp[r] = p * dp[r];
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {

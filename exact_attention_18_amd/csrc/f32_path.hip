@@ -246,7 +246,8 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
 }
 
 // delta: 16 threads per row, each summing 16-byte chunks part, part+16, ...
-template <typename T>
+// NEG stores -delta (the bf16 kernels start their dP accumulators from it).
+template <typename T, bool NEG>
 __global__ void __launch_bounds__(NT)
 rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restrict__ delta,
               long long rows, int d) {
@@ -278,14 +279,14 @@ rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restric
   acc += __shfl_xor(acc, 4);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 1);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (row < rows && part == 0) delta[row] = NEG ? -acc : acc;
 }
 
-template <typename T>
+template <typename T, bool NEG>
 hipError_t launch_rowdot(const T* o, const T* g, float* delta, long long rows, int d, hipStream_t s) {
   const long long blocks = (rows + (NT / 16) - 1) / (NT / 16);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rowdot_kernel<T>, dim3((unsigned)blocks), dim3(NT), 0, s, o, g, delta, rows, d);
+  hipLaunchKernelGGL((rowdot_kernel<T, NEG>), dim3((unsigned)blocks), dim3(NT), 0, s, o, g, delta, rows, d);
   return hipGetLastError();
 }
 
@@ -293,12 +294,12 @@ hipError_t launch_rowdot(const T* o, const T* g, float* delta, long long rows, i
 
 hipError_t launch_rowdot_bf16(const uint16_t* o, const uint16_t* dO, float* delta, long long rows,
                               int d, hipStream_t stream) {
-  return launch_rowdot<uint16_t>(o, dO, delta, rows, d, stream);
+  return launch_rowdot<uint16_t, true>(o, dO, delta, rows, d, stream);
 }
 
 hipError_t launch_rowdot_f32(const float* o, const float* dO, float* delta, long long rows, int d,
                              hipStream_t stream) {
-  return launch_rowdot<float>(o, dO, delta, rows, d, stream);
+  return launch_rowdot<float, false>(o, dO, delta, rows, d, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

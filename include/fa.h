@@ -221,7 +221,8 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  * launch when each of the two grids fits on the device at once, so that the
  * two kinds of workgroup share the compute units; the arithmetic per output
  * is the same either way.)  Arguments mean what they mean for fa_backward.
- *   fa_backward_preprocess: workspace rows delta_i = sum_c dO_ic * O_ic.
+ *   fa_backward_preprocess: workspace rows -delta_i, the negated row sums
+ *     delta_i = sum_c dO_ic * O_ic.
  *   fa_backward_dkdv: dK and dV, one workgroup per 128 keys, looping over
  *     query tiles (reads q, k, v, lse, dO and the workspace).
  *   fa_backward_dq: dQ, one workgroup per 128 queries, looping over key
