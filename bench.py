@@ -185,15 +185,15 @@ def main():
          _products(w, 2)),
     ]
     if w.backward:
+        # The backward as fa_backward runs it at this size: dQ (computing
+        # -delta of its queries on the way), then dK/dV.
         kernels += [
-            ("bwd_preprocess", lambda: fa.fa_backward_preprocess(P["o"], P["do"], B, H, N, d, P["ws"], ws_bytes, sp),
-             0.0),
+            ("bwd_dq", lambda: fa.fa_backward_dq_delta(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"],
+                                                       B, H, N, d, causal, scale, P["ws"], ws_bytes, sp),
+             _products(w, 1)),
             ("bwd_dkdv", lambda: fa.fa_backward_dkdv(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dk"], P["dv"],
                                                      B, H, N, d, causal, scale, P["ws"], ws_bytes, sp),
              _products(w, 4)),
-            ("bwd_dq", lambda: fa.fa_backward_dq(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dq"], B, H, N, d,
-                                                 causal, scale, P["ws"], ws_bytes, sp),
-             _products(w, 1)),
         ]
     step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
 

@@ -35,6 +35,7 @@ __all__ = [
     "fa_backward_preprocess",
     "fa_backward_dkdv",
     "fa_backward_dq",
+    "fa_backward_dq_delta",
     "fa_backward_workspace_size",
     "fa_backward_stored_ds",
     "fa_backward_stored_ds_workspace_size",
@@ -126,6 +127,11 @@ def fa_backward_dkdv(q, k, v, lse, do, dk, dv, B, H, N, d, causal, scale, ws, ws
 
 def fa_backward_dq(q, k, v, lse, do, dq, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
     return _call("fa_backward_dq", q, k, v, lse, do, dq, B, H, N, d, int(causal), float(scale), ws,
+                 ws_bytes, stream)
+
+
+def fa_backward_dq_delta(q, k, v, o, lse, do, dq, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_dq_delta", q, k, v, o, lse, do, dq, B, H, N, d, int(causal), float(scale), ws,
                  ws_bytes, stream)
 
 

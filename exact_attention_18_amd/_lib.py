@@ -37,6 +37,7 @@ SIGNATURES = {
     "fa_backward_preprocess": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "fa_backward_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_backward_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "fa_backward_dq_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_backward_workspace_size": (_sz, [_i, _i, _i, _i]),
     "fa_backward_stored_ds_workspace_size": (_sz, [_i, _i, _i, _i]),
     "fa_backward_stored_ds": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,

@@ -183,6 +183,19 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse
       N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
 }
 
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dO, void* dq, int B, int H, int N, int d, int causal, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  const void* in[6] = {q, k, v, o, lse, dO};
+  const size_t ib[6] = {0, 0, 0, 0, (size_t)B * H * N * sizeof(float), 0};
+  const void* out[1] = {dq};
+  int st = stage_checks(B, H, N, d, causal, scale, in, ib, 6, out, 1, workspace, workspace_bytes, true);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_bwd_dq_delta_bf16(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<float*>(workspace),
+      static_cast<uint16_t*>(dq), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+}
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 

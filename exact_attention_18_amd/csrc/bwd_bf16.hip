@@ -6,9 +6,10 @@
 // With P = exp(scale*Q K^T - LSE) (masked entries 0) and delta = rowsum(dO * O):
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),
 //     dQ = scale * dS K,   dK = scale * dS^T Q.
-// Three launches on one stream, no atomics, so the result is bit-reproducible:
+// Launches on one stream, no atomics, so the result is bit-reproducible:
 //   1. -delta (row-dot pre-pass, in f32_path.hip; the negated sums let the
-//      dP accumulators start from them);
+//      dP accumulators start from them), or computed by the dQ kernel for
+//      its own queries when that kernel runs first;
 //   2. dK/dV: one workgroup per (batch*head, 128 keys); each wave owns 32
 //      keys (K rows in registers) and loops over query tiles of 32 (causal:
 //      from the diagonal on);
@@ -173,8 +174,10 @@ struct DqLds {
 // One LDS buffer, big enough for either kernel's tiles, used by every
 // backward kernel of one head dimension.
 template <int D>
+constexpr int bwd_lds_elems() { return DkdvLds<D>::ELEMS > DqLds<D>::ELEMS ? DkdvLds<D>::ELEMS : DqLds<D>::ELEMS; }
+template <int D>
 __device__ __forceinline__ uint16_t* bwd_lds() {
-  constexpr int E = DkdvLds<D>::ELEMS > DqLds<D>::ELEMS ? DkdvLds<D>::ELEMS : DqLds<D>::ELEMS;
+  constexpr int E = bwd_lds_elems<D>();
   __shared__ __attribute__((aligned(16))) uint16_t buf[E];
   return buf;
 }
@@ -404,12 +407,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, bool CAUSAL>
+// DELTA: the workgroup first computes -delta of its own queries from O and
+// dO (the row-dot pre-pass's arithmetic, in the same order, so the values
+// are the same bits), writes it to nd_out for the dK/dV kernel that runs
+// next, and uses it itself; `delta` is then not read.
+template <int D, bool CAUSAL, bool DELTA = false>
 __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q,
                                          const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                          const float* __restrict__ LSE, const uint16_t* __restrict__ dO,
                                          const float* __restrict__ delta, uint16_t* __restrict__ dQ, int N,
-                                         int nqb, int total, float c, float scale) {
+                                         int nqb, int total, float c, float scale,
+                                         const uint16_t* __restrict__ O = nullptr, float* __restrict__ nd_out = nullptr) {
   using L = DqLds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
   uint16_t* smem = bwd_lds<D>();
@@ -442,7 +450,44 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
   const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
   // -delta of this lane's query (the workspace holds -delta): the dP^T
   // accumulators start from it
-  const float ndl = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+  float ndl;
+  if constexpr (DELTA) {
+    // 16 lanes per row, 16 rows per pass; the values go to HBM for the dK/dV
+    // kernel and, through LDS past the tiles, to the lanes that own the rows.
+    static_assert(DqLds<D>::ELEMS + 2 * Q_BLK <= bwd_lds_elems<D>(), "no room for the row sums");
+    float* nds = reinterpret_cast<float*>(smem + DqLds<D>::ELEMS);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
+    const int part = tid & 15;
+#pragma unroll
+    for (int it = 0; it < Q_BLK / (NT / 16); ++it) {
+      const int rl = it * (NT / 16) + (tid >> 4), row = q0 + rl;
+      float acc = 0.f;
+      if (row < N) {
+        for (int col = part * 8; col < D; col += 128) {
+          const u32x4 a = buf_load16(ors, (uint32_t)((row * D + col) * 2));
+          const u32x4 b = buf_load16(grs, (uint32_t)((row * D + col) * 2));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), acc);
+            acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), acc);
+          }
+        }
+      }
+      acc += __shfl_xor(acc, 8);
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 1);
+      if (part == 0) {
+        if (row < N) nd_out[(size_t)bh * N + row] = -acc;
+        nds[rl] = row < N ? -acc : 0.f;
+      }
+    }
+    __syncthreads();
+    ndl = nds[wave * 32 + l32];
+  } else {
+    ndl = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
+  }
   f32x16 ndv;
 #pragma unroll
   for (int r = 0; r < 16; ++r) ndv[r] = ndl;
@@ -533,6 +578,17 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ dO, const float* __restrict__ delta,
               uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
   dq_block<D, CAUSAL>(blockIdx.x, Q, K, V, LSE, dO, delta, dQ, N, nqb, total, c, scale);
+}
+
+// dQ together with -delta of its own queries (see dq_block); the dK/dV
+// kernel launched after it on the same stream reads that -delta.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>(), bwd_waves_per_simd<D>())))
+bwd_dq_delta_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                    const uint16_t* __restrict__ V, const float* __restrict__ LSE,
+                    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, float* __restrict__ nd_out,
+                    uint16_t* __restrict__ dQ, int N, int nqb, int total, float c, float scale) {
+  dq_block<D, CAUSAL, true>(blockIdx.x, Q, K, V, LSE, dO, nullptr, dQ, N, nqb, total, c, scale, O, nd_out);
 }
 
 // dK/dV and dQ in one launch: ids 16j .. 16j+7 run dK/dV block 8j + (id % 8)
@@ -680,6 +736,18 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 }
 
 template <int D, bool CAUSAL>
+hipError_t launch_dq_delta(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                           const uint16_t* dO, const uint16_t* o, float* nd, uint16_t* dq, int BH, int N,
+                           float scale, hipStream_t stream) {
+  const int nqb = (N + Q_BLK - 1) / Q_BLK;
+  const long long tq = (long long)BH * nqb;
+  if (tq > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((bwd_dq_delta_kernel<D, CAUSAL>), dim3((unsigned)tq), dim3(NT), 0, stream, q, k, v, lse,
+                     dO, o, nd, dq, N, nqb, (int)tq, score_coef(scale), scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 hipError_t launch_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
                      const uint16_t* dO, const float* delta, uint16_t* dq, int BH, int N, float scale,
                      hipStream_t stream) {
@@ -703,6 +771,18 @@ hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint
   if (d == 128)
     return causal ? launch_dkdv<128, true>(q, k, v, lse, dO, delta, dk, dv, BH, N, scale, stream)
                   : launch_dkdv<128, false>(q, k, v, lse, dO, delta, dk, dv, BH, N, scale, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                   const float* lse, const uint16_t* dO, float* delta, uint16_t* dq, int BH,
+                                   int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_dq_delta<64, true>(q, k, v, lse, dO, o, delta, dq, BH, N, scale, stream)
+                  : launch_dq_delta<64, false>(q, k, v, lse, dO, o, delta, dq, BH, N, scale, stream);
+  if (d == 128)
+    return causal ? launch_dq_delta<128, true>(q, k, v, lse, dO, o, delta, dq, BH, N, scale, stream)
+                  : launch_dq_delta<128, false>(q, k, v, lse, dO, o, delta, dq, BH, N, scale, stream);
   return hipErrorInvalidValue;
 }
 
@@ -738,21 +818,25 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
                            float scale, float* delta, hipStream_t stream) {
-  hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
-  if (e != hipSuccess) return e;
   // While each kernel's grid fits on the chip at once (256 CUs x the waves
   // per SIMD), the two run better side by side in one launch than one after
   // the other; beyond that the separate launches are faster.
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
   const long long blocks = (long long)BH * ((N + KV_BLK - 1) / KV_BLK);
-  if (d == 64 && blocks <= 256 * bwd_waves_per_simd<64>())
-    return causal ? launch_fused<64, true>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream)
-                  : launch_fused<64, false>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
-  if (d == 128 && blocks <= 256 * bwd_waves_per_simd<128>())
+  if (blocks <= 256 * (d == 64 ? bwd_waves_per_simd<64>() : bwd_waves_per_simd<128>())) {
+    hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
+    if (e != hipSuccess) return e;
+    if (d == 64)
+      return causal ? launch_fused<64, true>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream)
+                    : launch_fused<64, false>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
     return causal ? launch_fused<128, true>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream)
                   : launch_fused<128, false>(q, k, v, lse, dO, delta, dq, dk, dv, BH, N, scale, stream);
-  e = launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, BH, N, d, causal, scale, stream);
+  }
+  // Larger grids: dQ first, computing -delta on the way (no row-dot pass),
+  // then dK/dV.
+  hipError_t e = launch_bwd_dq_delta_bf16(q, k, v, o, lse, dO, delta, dq, BH, N, d, causal, scale, stream);
   if (e != hipSuccess) return e;
-  return launch_bwd_dq_bf16(q, k, v, lse, dO, delta, dq, BH, N, d, causal, scale, stream);
+  return launch_bwd_dkdv_bf16(q, k, v, lse, dO, delta, dk, dv, BH, N, d, causal, scale, stream);
 }
 
 }  // namespace fa

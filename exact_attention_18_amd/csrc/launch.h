@@ -73,6 +73,9 @@ hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint
                                 uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
                                 float scale, hipStream_t stream);
 
+hipError_t launch_bwd_dq_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                   const float* lse, const uint16_t* dO, float* delta, uint16_t* dq, int BH,
+                                   int N, int d, bool causal, float scale, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                               const float* lse, const uint16_t* dO, const float* delta,
                               uint16_t* dq, int BH, int N, int d, bool causal, float scale,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 enum fa_status {
   FA_OK = 0,
@@ -213,20 +213,27 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages of fa_backward, as separate calls (bf16 only).  Calling
- * fa_backward_preprocess, then fa_backward_dkdv and fa_backward_dq (in either
- * order) on one stream with the same workspace gives exactly what
- * fa_backward gives; they exist so that callers can time or schedule the
- * stages one by one.  (fa_backward itself runs the dK/dV and dQ work in one
- * launch when each of the two grids fits on the device at once, so that the
- * two kinds of workgroup share the compute units; the arithmetic per output
- * is the same either way.)  Arguments mean what they mean for fa_backward.
+ * The stages of fa_backward, as separate calls (bf16 only), so that callers
+ * can time or schedule them one by one.  Either sequence on one stream with
+ * the same workspace gives exactly what fa_backward gives:
+ *   fa_backward_dq_delta, then fa_backward_dkdv (what fa_backward runs when
+ *   the grids are large), or
+ *   fa_backward_preprocess, then fa_backward_dkdv and fa_backward_dq in
+ *   either order.
+ * (For grids that fit on the device at once fa_backward runs the dK/dV and
+ * dQ work in one launch, so that the two kinds of workgroup share the
+ * compute units; the arithmetic per output is the same in every case.)
+ * Arguments mean what they mean for fa_backward.
  *   fa_backward_preprocess: workspace rows -delta_i, the negated row sums
  *     delta_i = sum_c dO_ic * O_ic.
  *   fa_backward_dkdv: dK and dV, one workgroup per 128 keys, looping over
  *     query tiles (reads q, k, v, lse, dO and the workspace).
  *   fa_backward_dq: dQ, one workgroup per 128 queries, looping over key
  *     tiles (reads q, k, v, lse, dO and the workspace).
+ *   fa_backward_dq_delta: dQ as fa_backward_dq, but each workgroup first
+ *     computes -delta of its own queries from o and dO (the same values
+ *     fa_backward_preprocess writes) and writes them to the workspace, so no
+ *     preprocess pass is needed.
  * The same checks as fa_backward apply to every buffer each stage touches.
  */
 int fa_backward_preprocess(const void* o, const void* dO, int B, int H, int N, int d,
@@ -238,6 +245,10 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const float* l
 int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse,
                    const void* dO, void* dq, int B, int H, int N, int d, int causal, float scale,
                    const void* workspace, size_t workspace_bytes, void* stream);
+int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dO, void* dq, int B, int H, int N, int d,
+                         int causal, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Bytes of workspace fa_backward and fa_backward_f32 need for these sizes
  * (0 if a size is not positive).  Pure host function. */

@@ -276,7 +276,8 @@ STAGE_SHAPES = [(1, 16, 2048, 128, True), (2, 16, 2048, 128, True), (2, 16, 2048
 def test_backward_equals_its_stages(fa, B, H, N, d, causal):
     """fa_backward (one launch for both passes on small grids, two on large
     ones) gives the same bits as fa_backward_preprocess, fa_backward_dkdv and
-    fa_backward_dq called one by one; sampled heads agree with the oracle."""
+    fa_backward_dq called one by one, and as fa_backward_dq_delta followed by
+    fa_backward_dkdv; sampled heads agree with the oracle."""
     import torch
 
     q, k, v, do = random_inputs(500 + N + B, (B, H, N, d), "bf16", 4)
@@ -294,9 +295,23 @@ def test_backward_equals_its_stages(fa, B, H, N, d, causal):
     assert fa.fa_backward_dkdv(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), lse.data_ptr(), tdo.data_ptr(),
                                staged[1].data_ptr(), staged[2].data_ptr(), B, H, N, d, causal, scale,
                                ws.data_ptr(), nb, sp) == 0
+    # the other sequence: dQ computing -delta itself, into a NaN-filled
+    # workspace (so dK/dV can only have read what that pass wrote), then dK/dV
+    ws2 = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device=tq.device)
+    staged2 = [torch.full_like(tq, float("nan")) for _ in range(3)]
+    assert fa.fa_backward_dq_delta(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   tdo.data_ptr(), staged2[0].data_ptr(), B, H, N, d, causal, scale,
+                                   ws2.data_ptr(), nb, sp) == 0
+    assert fa.fa_backward_dkdv(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), lse.data_ptr(), tdo.data_ptr(),
+                               staged2[1].data_ptr(), staged2[2].data_ptr(), B, H, N, d, causal, scale,
+                               ws2.data_ptr(), nb, sp) == 0
     torch.cuda.synchronize()
-    for name, a, b in zip(("dQ", "dK", "dV"), whole, staged):
+    for name, a, b, c2 in zip(("dQ", "dK", "dV"), whole, staged, staged2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+        assert torch.equal(a.view(torch.int16), c2.view(torch.int16)), name + " (dq_delta order)"
+    # both sequences leave the same -delta rows in the workspace
+    rows = B * H * N
+    assert torch.equal(ws.view(torch.float32)[:rows], ws2[:rows])
     got = [host64(t) for t in whole]
     for (b, h) in sorted({(0, 0), (B - 1, H - 1)}):
         sl = (slice(b, b + 1), slice(h, h + 1))
