@@ -338,3 +338,65 @@ def test_stored_ds_rejects_overlaps_and_small_workspace(lib):
     assert bwd_ds(lib, ws_bytes=need - 1) == INVALID
     # the workspace must hold the dS^T part too, not only fa_backward's part
     assert bwd_ds(lib, ws_bytes=lib.fa_backward_workspace_size(1, 1, 8, 64)) == INVALID
+
+
+# The stages of fa_backward: name -> (number of leading pointer arguments,
+# whether causal and scale follow the sizes, indices of the outputs among
+# those pointers).  The workspace pointer comes after the sizes.
+STAGES = {
+    "fa_backward_preprocess": (2, False, ()),
+    "fa_backward_dkdv": (7, True, (5, 6)),
+    "fa_backward_dq": (6, True, (5,)),
+    "fa_backward_dq_delta": (7, True, (6,)),
+}
+
+
+def stage(lib, name, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None, ws=None, ws_bytes=None):
+    n, has_cs, _ = STAGES[name]
+    p = ptrs or [ptr(i) for i in range(n)]
+    w = ptr(n) if ws is None else ws
+    if ws_bytes is None:
+        ws_bytes = lib.fa_backward_workspace_size(B, H, N, d)
+    fn = getattr(lib, name)
+    if has_cs:
+        return fn(*p, B, H, N, d, causal, scale, w, ws_bytes, None)
+    return fn(*p, B, H, N, d, w, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", sorted(STAGES))
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=-1), dict(d=0), dict(causal=2), dict(scale=math.nan)])
+def test_backward_stages_reject_bad_sizes(lib, name, kw):
+    if not STAGES[name][1] and ("causal" in kw or "scale" in kw):
+        pytest.skip("this stage takes no causal flag or scale")
+    assert stage(lib, name, **kw) == INVALID
+
+
+@pytest.mark.parametrize("name", sorted(STAGES))
+def test_backward_stages_reject_null_misaligned_and_small_workspace(lib, name):
+    n = STAGES[name][0]
+    for which in range(n):
+        p = [ptr(i) for i in range(n)]
+        p[which] = None
+        assert stage(lib, name, ptrs=p) == INVALID, which
+        p = [ptr(i) for i in range(n)]
+        p[which] = ptr(which, 4)
+        assert stage(lib, name, ptrs=p) == INVALID, which
+    assert stage(lib, name, ws=0) == INVALID
+    need = lib.fa_backward_workspace_size(1, 1, 8, 64)
+    assert stage(lib, name, ws_bytes=need - 1) == INVALID
+
+
+@pytest.mark.parametrize("name", ["fa_backward_dkdv", "fa_backward_dq", "fa_backward_dq_delta"])
+def test_backward_stages_reject_outputs_on_inputs_or_workspace(lib, name):
+    n, _, outs = STAGES[name]
+    for o in outs:
+        p = [ptr(i) for i in range(n)]
+        p[o] = p[0] + 64  # output starts inside q
+        assert stage(lib, name, ptrs=p) == INVALID
+        p = [ptr(i) for i in range(n)]
+        assert stage(lib, name, ptrs=p, ws=p[o]) == INVALID  # workspace on an output
+
+
+@pytest.mark.parametrize("name", ["fa_backward_dkdv", "fa_backward_dq", "fa_backward_dq_delta"])
+def test_backward_stages_reject_unsupported_head_dim(lib, name):
+    assert stage(lib, name, d=100) == UNSUP
