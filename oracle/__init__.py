@@ -5,6 +5,7 @@ the benchmark's CPU-baseline leg, never by the GPU library.
 """
 from .attention import (  # noqa: F401
     attention_backward,
+    attention_backward_dq_rows,
     attention_forward,
     attention_forward_block_sparse,
     attention_forward_block_sparse_rows,

@@ -46,6 +46,7 @@ __all__ = [
     "attention_forward",
     "attention_forward_rows",
     "attention_backward",
+    "attention_backward_dq_rows",
     "block_visibility",
     "attention_forward_block_sparse",
     "attention_forward_block_sparse_rows",
@@ -159,6 +160,24 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_backward_dq_rows(q_bh, k_bh, v_bh, do_bh, rows, causal: bool, scale: float):
+    """dQ of ``attention_backward`` restricted to some query rows of one
+    (batch, head).
+
+    Row i of dQ needs only row i of P, dP and dS (dS_i = P_i * (dP_i -
+    rowsum(P_i * dP_i)), dQ_i = scale * dS_i K), so this is the same
+    definition evaluated for the listed rows.  Inputs are [N, d]; returns
+    dQ [len(rows), d].
+    """
+    rows = np.asarray(rows)
+    k, v = _f64(k_bh), _f64(v_bh)
+    s = scores(_f64(q_bh)[rows], k, causal, scale, rows=rows)
+    p, _ = softmax_rows(s)
+    dp = _f64(do_bh)[rows] @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+    return scale * (ds @ k)
 
 
 def block_visibility(block_mask: np.ndarray, n: int, block: int) -> np.ndarray:

@@ -320,6 +320,45 @@ def test_backward_equals_its_stages(fa, B, H, N, d, causal):
             e = max_abs(g[sl], r)
             assert e <= TOL_BF16, f"{name} head {(b, h)}: {e:.4g} (storage floor {storage_floor(r):.3g})"
 
+
+@pytest.mark.parametrize("N,causal", [(131072, True), (65536, False)])
+def test_long_sequence_forward(fa, N, causal):
+    """One head of a long sequence (1024-2048 key tiles per row block):
+    sampled rows of O and LSE against the oracle."""
+    q, k, v = random_inputs(900 + N, (1, 1, N, 128), "bf16", 3)
+    scale = 128 ** -0.5
+    o, lse = _run_fwd(fa, q, k, v, causal, scale)
+    rows = _sample_rows(N, 12, np.random.default_rng(N))
+    ro, rl = oracle.attention_forward_rows(fi.exact_f64(q[0, 0]), fi.exact_f64(k[0, 0]), fi.exact_f64(v[0, 0]),
+                                           rows, causal, scale)
+    assert max_abs(host64(o)[0, 0, rows], ro) <= TOL_BF16
+    assert max_abs(host64(lse)[0, 0, rows], rl) <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_sequence_backward(fa, causal):
+    """One head, N = 32768: sampled rows of dQ against the oracle, and two
+    identities of the backward over all rows: sum_j dK_j = 0 (every row of dS
+    sums to zero) and sum_j dV_j = sum_i dO_i (every row of P sums to one),
+    within the rounding of the bf16-stored gradients."""
+    import torch
+
+    N, d = 32768, 128
+    q, k, v, do = random_inputs(950 + int(causal), (1, 1, N, d), "bf16", 4)
+    scale = d ** -0.5
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(tq, tk, tv, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(N, 10, np.random.default_rng(N + int(causal)))
+    rdq = oracle.attention_backward_dq_rows(*(fi.exact_f64(a[0, 0]) for a in (q, k, v, do)), rows, causal, scale)
+    assert max_abs(host64(dq)[0, 0, rows], rdq) <= TOL_BF16
+    gk, gv = host64(dk)[0, 0], host64(dv)[0, 0]
+    # each stored value is within 2^-9 of its own magnitude of the exact one
+    assert np.all(np.abs(gk.sum(0)) <= 2.0 ** -9 * np.abs(gk).sum(0) + 1e-3)
+    dsum = fi.exact_f64(do)[0, 0].sum(0)
+    assert np.all(np.abs(gv.sum(0) - dsum) <= 2.0 ** -9 * np.abs(gv).sum(0) + 1e-3)
+
 def test_forward_is_deterministic_across_streams(fa):
     import torch
 

@@ -53,6 +53,18 @@ def test_forward_rows_equals_full():
         assert np.array_equal(lse[0, 0, rows], lrow)
 
 
+def test_backward_dq_rows_equals_full():
+    """The row-restricted dQ is the full backward's dQ on those rows (the full
+    backward is pinned by finite differences and the softmax identities)."""
+    r = np.random.default_rng(16)
+    q, k, v, do = (r.standard_normal((1, 1, 40, 8)) for _ in range(4))
+    rows = np.array([0, 1, 17, 38, 39])
+    for causal in (False, True):
+        dq, _, _ = oracle.attention_backward(q, k, v, do, causal, 0.3)
+        dqr = oracle.attention_backward_dq_rows(q[0, 0], k[0, 0], v[0, 0], do[0, 0], rows, causal, 0.3)
+        assert np.allclose(dq[0, 0, rows], dqr, rtol=1e-12, atol=1e-12)
+
+
 def test_block_sparse_rows_equals_full():
     r = np.random.default_rng(8)
     q, k, v = (r.standard_normal((1, 1, 40, 8)) for _ in range(3))
