@@ -205,37 +205,54 @@ struct Fp8Lds {
   static constexpr int BYTES = 2 * STAGE;
 };
 
-// Global -> register staging of one tile: 32 bytes of K and of V^T, and one
-// word of the K or V scales, per thread.
-struct Fp8TileRegs {
-  u32x4 k0, k1, v0, v1;
-  uint32_t e;
-};
-
-__device__ __forceinline__ void fp8_load_tile(Fp8TileRegs& r, __amdgpu_buffer_rsrc_t k8, __amdgpu_buffer_rsrc_t ke,
-                                              __amdgpu_buffer_rsrc_t v8, __amdgpu_buffer_rsrc_t ve, int kv0, int tid) {
-  const uint32_t koff = (uint32_t)((kv0 + (tid >> 2)) * FD + (tid & 3) * 32);
-  r.k0 = buf_load16(k8, koff);
-  r.k1 = buf_load16(k8, koff + 16);
-  const uint32_t voff = (uint32_t)((kv0 / FBC) * FD * 64 + (tid >> 1) * 64 + (tid & 1) * 32);
-  r.v0 = buf_load16(v8, voff);
-  r.v1 = buf_load16(v8, voff + 16);
-  r.e = tid < 64 ? __builtin_amdgcn_raw_buffer_load_b32(ke, (uint32_t)((kv0 + tid) * 4), 0, 0)
-                 : tid < 128 ? __builtin_amdgcn_raw_buffer_load_b32(ve, (uint32_t)((kv0 / FBC) * 256 + (tid - 64) * 4), 0, 0)
-                             : 0u;
-}
-
-__device__ __forceinline__ void fp8_store_tile(const Fp8TileRegs& r, uint8_t* st, int tid) {
+// One tile (K codes, K scales, V^T codes, V scales) by direct HBM -> LDS
+// loads: each 16-byte load puts lane l's chunk 16 l bytes after its base, so
+// the K rows (9 chunks each, 8 of data) take 9 loads and the V^T rows (5
+// chunks, 4 of data) 10; lanes on padding get an offset past the buffer
+// (zeros).  Each scale block is one 4-byte load.  Load j of the 21 is issued
+// by wave j % 4.
+struct Fp8TileDma {
   using L = Fp8Lds;
-  uint8_t* kd = st + (tid >> 2) * L::KSTR + (tid & 3) * 32;
-  *reinterpret_cast<u32x4*>(kd) = r.k0;
-  *reinterpret_cast<u32x4*>(kd + 16) = r.k1;
-  uint8_t* vd = st + L::K_BYTES + L::KE_BYTES + (tid >> 1) * L::VSTR + (tid & 1) * 32;
-  *reinterpret_cast<u32x4*>(vd) = r.v0;
-  *reinterpret_cast<u32x4*>(vd + 16) = r.v1;
-  if (tid < 64) reinterpret_cast<uint32_t*>(st + L::K_BYTES)[tid] = r.e;
-  else if (tid < 128) reinterpret_cast<uint32_t*>(st + L::K_BYTES + L::KE_BYTES + L::V_BYTES)[tid - 64] = r.e;
-}
+  static constexpr int KL = FBC * L::KSTR / 1024, VL = FD * L::VSTR / 1024;
+  static_assert(KL * 1024 == FBC * L::KSTR && VL * 1024 == FD * L::VSTR, "tiles must be whole loads");
+  static constexpr int NL = KL + 1 + VL + 1, PW = (NL + 3) / 4;
+  uint32_t voff[PW];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + 4 * u;
+      uint32_t o = 0x80000000u;
+      if (j < KL) {
+        const int p = 64 * j + lane, row = p / (L::KSTR / 16), col = p % (L::KSTR / 16);
+        if (col < FD / 16) o = (uint32_t)(row * FD + col * 16);
+      } else if (j == KL || j == NL - 1) {
+        o = (uint32_t)lane * 4;
+      } else if (j < NL) {
+        const int p = 64 * (j - KL - 1) + lane, row = p / (L::VSTR / 16), col = p % (L::VSTR / 16);
+        if (col < 4) o = (uint32_t)(row * 64 + col * 16);
+      }
+      voff[u] = o;
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t k8, __amdgpu_buffer_rsrc_t ke,
+                                        __amdgpu_buffer_rsrc_t v8, __amdgpu_buffer_rsrc_t ve, int kv0, uint8_t* st,
+                                        int wave) const {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + 4 * u;
+      if (j < KL)
+        lds_load16(k8, reinterpret_cast<uint16_t*>(st + 1024 * j), voff[u] + (uint32_t)kv0 * FD);
+      else if (j == KL)
+        lds_load4(ke, reinterpret_cast<uint16_t*>(st + L::K_BYTES), voff[u] + (uint32_t)kv0 * 4);
+      else if (j < NL - 1)
+        lds_load16(v8, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + 1024 * (j - KL - 1)),
+                   voff[u] + (uint32_t)(kv0 / FBC) * FD * 64);
+      else if (j == NL - 1)
+        lds_load4(ve, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + L::V_BYTES),
+                  voff[u] + (uint32_t)(kv0 / FBC) * 256);
+    }
+  }
+};
 
 // One 64-key tile for this wave's 32 queries (same online softmax as the
 // bf16 forward; see fwd_bf16.hip).
@@ -332,8 +349,11 @@ __device__ __forceinline__ void fp8_tile_step(const uint8_t* st, const v8i* qf, 
 #undef FA_FP8_PV
 }
 
+// Three waves per SIMD: with the tiles loaded straight into LDS a wave
+// needs ~160 VGPRs and a workgroup 40 KB of LDS (measured 10-12% faster than
+// two waves per SIMD with register-staged tiles).
 template <bool CAUSAL>
-__global__ void __launch_bounds__(FNT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(FNT) __attribute__((amdgpu_waves_per_eu(3, 3)))
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QE, const uint8_t* __restrict__ K8,
                const uint8_t* __restrict__ KE, const uint8_t* __restrict__ V8, const uint8_t* __restrict__ VE,
                uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int Np, int nqb, int total, float c) {
@@ -373,21 +393,22 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QE, c
   for (int i = 0; i < FD / 32; ++i) oacc[i] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
 
-  Fp8TileRegs regs;
-  fp8_load_tile(regs, krs, kes, vrs, ves, 0, tid);
-  fp8_store_tile(regs, smem, tid);
+  Fp8TileDma dma;
+  dma.init(wave, lane);
+  dma.issue(krs, kes, vrs, ves, 0, smem, wave);
+  wait_vmem();
   __syncthreads();
   const int n_plain = min(CAUSAL ? q0 / FBC : ntiles, N / FBC);
   auto step = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint8_t* st = smem + (j & 1) * L::STAGE;
     const int kv0 = j * FBC;
-    if (j + 1 < ntiles) fp8_load_tile(regs, krs, kes, vrs, ves, kv0 + FBC, tid);
+    if (j + 1 < ntiles) dma.issue(krs, kes, vrs, ves, kv0 + FBC, smem + ((j + 1) & 1) * L::STAGE, wave);
     if (!MASK || !CAUSAL || kv0 <= qw + 31) {
       const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * h;
       fp8_tile_step<MASK>(st, qf, qsc, oacc, m, lsum, c, lim, lane);
     }
-    if (j + 1 < ntiles) fp8_store_tile(regs, smem + ((j + 1) & 1) * L::STAGE, tid);
+    wait_vmem();
     __syncthreads();
   };
   int j = 0;
