@@ -28,23 +28,6 @@ namespace {
 constexpr int DEC_NT = 256;             // 4 wavefronts, each its own chunk
 constexpr int DEC_WAVES = DEC_NT / 64;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over aligned groups of LPK (8 or 16) lanes; every lane of a group gets
-// the same bits (each step adds a pair of values in both orders, and float
-// addition is commutative).
-template <int LPK>
-__device__ __forceinline__ float group_sum(float x) {
-  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
-  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
-  x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
-  if constexpr (LPK == 16) x += dpp_mov<0x140>(x);  // row_mirror: i <-> 15 - i within 16
-  return x;
-}
-
 // a.lo*b.lo + a.hi*b.hi + acc for two bf16 pairs (v_dot2c_f32_bf16).
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc,

@@ -157,4 +157,21 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint16_t* ds
 // operations) are complete.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPK (8 or 16) lanes; every lane of a group gets
+// the same bits (each step adds a pair of values in both orders, and float
+// addition is commutative).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  x += dpp_mov<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+  if constexpr (LPK == 16) x += dpp_mov<0x140>(x);  // row_mirror: i <-> 15 - i within 16
+  return x;
+}
+
 }  // namespace fa

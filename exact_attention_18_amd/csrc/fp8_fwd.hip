@@ -79,59 +79,82 @@ __device__ __forceinline__ uint8_t e8m0(int t) {
   return (uint8_t)(b < 0 ? 0 : b > 254 ? 254 : b);
 }
 
-// One thread per row of Q or K (BH * Np rows); rows past N become zero.
+// Q or K rows (BH * Np of them; rows past N become zero), 4 lanes per row:
+// lane j holds elements 32j .. 32j+31, which is also its scale block, so each
+// row is one coalesced 256-byte load and one 128-byte store.  The arithmetic
+// is that of a serial pass over the row (sign flip, Walsh-Hadamard butterflies
+// of widths 1, 2, ..., 64 in that order, block maximum, rounding), so the
+// bytes are the same: widths 1 to 16 pair elements within a lane, widths 32
+// and 64 pair lane j with lane j ^ 1 and j ^ 2, the lower keeping a + b and
+// the upper a - b.
 __global__ void __launch_bounds__(256)
 fp8_quant_rows_kernel(const uint16_t* __restrict__ X, const float* __restrict__ signs, uint8_t* __restrict__ codes,
                       uint8_t* __restrict__ exps, int N, int Np, long long rows) {
-  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const long long bh = r / Np;
-  const int n = (int)(r - bh * Np);
-  float y[FD];
+  static_assert(FD == 128, "4 lanes of 32 elements per row");
+  __shared__ float sg[FD];  // the signs, read by every row's lanes
+  if (signs != nullptr && threadIdx.x < FD) sg[threadIdx.x] = signs[threadIdx.x];
+  __syncthreads();
+  const long long r = (long long)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int j = threadIdx.x & 3;
+  const bool live = r < rows;
+  const long long bh = live ? r / Np : 0;
+  const int n = live ? (int)(r - bh * Np) : N;
+  float y[32];
   if (n < N) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(X + (bh * N + n) * FD);
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + (bh * N + n) * FD + 32 * j);
 #pragma unroll
-    for (int i = 0; i < FD / 8; ++i) {
-      const u32x4 w = src[i];
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = src[c];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[8 * i + 2 * j] = bf16_lo(w[j]);
-        y[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+      for (int e = 0; e < 4; ++e) {
+        y[8 * c + 2 * e] = bf16_lo(w[e]);
+        y[8 * c + 2 * e + 1] = bf16_hi(w[e]);
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < FD; ++i) y[i] = 0.f;
+    for (int i = 0; i < 32; ++i) y[i] = 0.f;
   }
-  if (signs != nullptr && n < N) {  // rows past N stay +0 (no -0 from a negative sign)
+  if (signs != nullptr) {  // rows past N stay +0 (no sign flip, so no -0)
+    if (n < N) {
 #pragma unroll
-    for (int i = 0; i < FD; ++i) y[i] *= signs[i];
-    // Walsh-Hadamard butterfly, widths 1, 2, ..., 64: (a, b) -> (a + b, a - b).
+      for (int i = 0; i < 32; ++i) y[i] *= sg[32 * j + i];
+    }
 #pragma unroll
-    for (int h = 1; h < FD; h *= 2)
+    for (int h = 1; h < 32; h *= 2)
 #pragma unroll
-      for (int i = 0; i < FD; ++i)
+      for (int i = 0; i < 32; ++i)
         if ((i & h) == 0) {
           const float a = y[i], b = y[i + h];
           y[i] = a + b;
           y[i + h] = a - b;
         }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {  // width 32: lanes j ^ 1
+      const float o = dpp_mov<0xB1>(y[i]);
+      y[i] = (j & 1) ? o - y[i] : y[i] + o;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {  // width 64: lanes j ^ 2
+      const float o = dpp_mov<0x4E>(y[i]);
+      y[i] = (j & 2) ? o - y[i] : y[i] + o;
+    }
   }
-  uint32_t w[FD / 4];
-  uint32_t ex = 0;
+  float amax = 0.f;
 #pragma unroll
-  for (int blk = 0; blk < FD / 32; ++blk) {
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[32 * blk + i]));
-    const int t = block_exponent(amax);
-    quantize32(y + 32 * blk, t, w + 8 * blk);
-    ex |= (uint32_t)e8m0(t) << (8 * blk);
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
+  const int t = block_exponent(amax);
+  uint32_t w[8];
+  quantize32(y, t, w);
+  uint32_t ex = (uint32_t)e8m0(t) << (8 * j);
+  ex |= (uint32_t)__float_as_int(dpp_mov<0xB1>(__int_as_float((int)ex)));
+  ex |= (uint32_t)__float_as_int(dpp_mov<0x4E>(__int_as_float((int)ex)));
+  if (live) {
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + r * FD + 32 * j);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    if (j == 0) reinterpret_cast<uint32_t*>(exps)[r] = ex;
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(codes + r * FD);
-#pragma unroll
-  for (int i = 0; i < FD / 16; ++i) dst[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-  reinterpret_cast<uint32_t*>(exps)[r] = ex;
 }
 
 // One thread per (batch*head, 32-key block, 4 adjacent columns); column
@@ -454,7 +477,7 @@ hipError_t launch_fp8_prepare(const uint16_t* q, const uint16_t* k, const uint16
   const Fp8Buffer L = fp8_buffer_layout(BH, N);
   uint8_t* base = static_cast<uint8_t*>(buf);
   const long long rows = (long long)BH * L.Np;
-  const unsigned rb = (unsigned)((rows + 255) / 256);
+  const unsigned rb = (unsigned)((rows + 63) / 64);   // 64 rows per workgroup
   hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rb), dim3(256), 0, stream, q, signs, base + L.q8, base + L.qe, N,
                      L.Np, rows);
   hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rb), dim3(256), 0, stream, k, signs, base + L.k8, base + L.ke, N,
