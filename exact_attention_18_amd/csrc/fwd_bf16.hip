@@ -710,8 +710,9 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
 // and give bit-identical results.
 //
 // plan (int32): [0] items per head P, [1] partial slots per head, [2] mean,
-// then row_cnt[nqb], row_parts[nqb], row_first[nqb], row_slot[nqb],
-// item_qb[3 nqb], item_part[3 nqb].  With split iff cnt > 2 mean and
+// [3] number of split rows, then row_cnt[nqb], row_parts[nqb],
+// row_first[nqb], row_slot[nqb], item_qb[3 nqb], item_part[3 nqb],
+// split_qb[nqb] (the split rows, in order).  With split iff cnt > 2 mean and
 // parts = min(16, ceil(cnt / mean)): fewer than nqb / 2 rows split, so P < 2.5 nqb and
 // the split rows use fewer than 1.5 nqb slots (2 nqb are allocated).
 
@@ -729,6 +730,7 @@ sparse_plan_kernel(const uint8_t* __restrict__ bmask, int nqb, int causal, int* 
   int* slot = first + nqb;
   int* item_qb = slot + nqb;
   int* item_part = item_qb + 3 * nqb;
+  int* split_qb = item_part + 3 * nqb;
   for (int qb = threadIdx.x; qb < nqb; qb += 256) s_cnt[qb] = 0;
   __syncthreads();
   // Count the visible blocks of every row: the mask is read as a flat array,
@@ -753,19 +755,21 @@ sparse_plan_kernel(const uint8_t* __restrict__ bmask, int nqb, int causal, int* 
     long long total = 0;
     for (int qb = 0; qb < nqb; ++qb) total += s_cnt[qb];
     const int mean = (int)max(1LL, (total + nqb - 1) / nqb);
-    int P = 0, S = 0;
+    int P = 0, S = 0, ns = 0;
     for (int qb = 0; qb < nqb; ++qb) {
       const int c = s_cnt[qb];
       const int p = c > 2 * mean ? min(SPARSE_MAX_PARTS, (c + mean - 1) / mean) : 1;
       s_parts[qb] = p;
       s_first[qb] = P;
       slot[qb] = p > 1 ? S : -1;
+      if (p > 1) split_qb[ns++] = qb;
       P += p;
       if (p > 1) S += p;
     }
     plan[0] = P;
     plan[1] = S;
     plan[2] = mean;
+    plan[3] = ns;
   }
   __syncthreads();
   for (int qb = threadIdx.x; qb < nqb; qb += 256) {
@@ -939,13 +943,19 @@ template <int D>
 __global__ void __launch_bounds__(256)
 sparse_merge_kernel(const int* __restrict__ plan, const float* __restrict__ part_o,
                     const float* __restrict__ part_ml, uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
-                    int nqb) {
-  const int blk = blockIdx.x >> 2, quarter = blockIdx.x & 3;
-  const int bh = blk / nqb, qb = blk - bh * nqb;
+                    int nqb, int BH) {
+  // Items (head, split row, quarter of its 128 rows), walked by a grid of
+  // fixed size: only the split rows have anything to merge.
   const int* row_parts = plan + 4 + nqb;
   const int* row_slot = row_parts + 2 * nqb;
+  const int* split_qb = row_slot + nqb + 6 * nqb;
+  const int ns = plan[3];
+  const long long items = (long long)BH * ns * 4;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+  const int quarter = (int)(it & 3);
+  const long long hr = it >> 2;
+  const int bh = (int)(hr / ns), qb = split_qb[hr - (long long)bh * ns];
   const int parts = row_parts[qb];
-  if (parts == 1) return;
   const size_t s0 = (size_t)bh * 2 * nqb + row_slot[qb];
   constexpr int C4 = D / 4;
   for (int idx = threadIdx.x; idx < 32 * C4; idx += 256) {
@@ -981,6 +991,7 @@ sparse_merge_kernel(const int* __restrict__ plan, const float* __restrict__ part
     *reinterpret_cast<u32x2*>(O + ((size_t)bh * N + q) * D + c4) = w;
     if (c4 == 0) LSE[(size_t)bh * N + q] = Lsum > 0.f ? (M + log2_hw(Lsum)) * kLn2 : -INFINITY;
   }
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -1002,8 +1013,8 @@ hipError_t launch_sparse_balanced(const uint16_t* q, const uint16_t* k, const ui
   if (wgs >= 8) wgs &= ~7LL;   // a multiple of 8: the same number of workgroups per XCD
   hipLaunchKernelGGL((fwd_sparse_balanced_kernel<D, CAUSAL>), dim3((unsigned)wgs), dim3(NT), 0, stream, q, k, v, o,
                      lse, N, nqb, BH, score_coef(scale), bmask, plan, po, pml, counters);
-  hipLaunchKernelGGL((sparse_merge_kernel<D>), dim3((unsigned)((long long)BH * nqb * 4)), dim3(256), 0, stream, plan,
-                     po, pml, o, lse, N, nqb);
+  const unsigned mwgs = (unsigned)min((long long)BH * nqb * 4, 1024LL);
+  hipLaunchKernelGGL((sparse_merge_kernel<D>), dim3(mwgs), dim3(256), 0, stream, plan, po, pml, o, lse, N, nqb, BH);
   return hipGetLastError();
 }
 
@@ -1024,7 +1035,7 @@ SparseWorkspace sparse_workspace_layout(long long BH, int N, int d) {
   const long long nqb = (N + BR - 1) / BR;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   w.plan = 0;
-  w.counters = up((size_t)(4 + 4 * nqb + 6 * nqb) * sizeof(int));
+  w.counters = up((size_t)(4 + 4 * nqb + 6 * nqb + nqb) * sizeof(int));
   w.part_o = up(w.counters + 8 * sizeof(int));
   w.part_ml = up(w.part_o + (size_t)BH * 2 * nqb * BR * d * sizeof(float));
   w.bytes = up(w.part_ml + (size_t)BH * 2 * nqb * BR * 2 * sizeof(float));
