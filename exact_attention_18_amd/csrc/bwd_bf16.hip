@@ -53,10 +53,24 @@ constexpr int bwd_waves_per_simd() { return D == 64 ? 3 : 2; }
 
 // Row stride (elements) of a tile that is read both with 16-byte row reads
 // (32 rows, one column block) and with the transpose read (4 rows x 32
-// bytes per 16 lanes): 48 bytes (d=128) or 144 bytes (d=64) past a multiple
-// of 256 keeps both patterns free of bank conflicts.
+// bytes per 16 lanes).  The row reads are free of bank conflicts when 16
+// consecutive rows start on 16 different 16-byte slots of a 256-byte bank
+// line; 304 bytes (d=128) and 144 bytes (d=64) do that.  No stride also
+// keeps 4 consecutive rows of a transpose read apart, so those reads take
+// rows 4 apart instead (spread_row): rows x, x+4, x+8, x+12 start 0, 64,
+// 128 and 192 bytes apart in the bank line at either stride.
 template <int D>
 constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
+
+// Tile row that holds row x = 16t + 8s + 4g + j of a 32x32 MFMA operand
+// (j = 0..3 the 4 rows one lane group of the transpose read covers, g the
+// lane half, s the second read of the pair, t the half of a 32-row block):
+// 16t + 4j + 2s + g, so one transpose read takes rows 4 apart.  Row reads
+// use the same map (lane x reads tile row spread_row(x)), which keeps the
+// accumulators of S and dP in the order the transpose reads expect.
+__device__ __forceinline__ constexpr int spread_row(int x) {
+  return (x & 16) | ((x & 3) << 2) | ((x >> 2) & 2) | ((x >> 2) & 1);
+}
 // Row stride of a tile read only with 16-byte row reads.
 template <int D>
 constexpr int row_read_stride() { return D + 8; }
@@ -102,6 +116,16 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int row0, int
   const uint16_t* p = tile + (row0 + 16 * t + 4 * g + ((lane & 15) >> 2)) * STRIDE + col0 +
                       16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   return bf16x8_from(lds_read_tr16(p), lds_read_tr16(p + 8 * STRIDE));
+}
+
+// tr_operand over a tile whose 32-row blocks are in spread_row order: slot v
+// of lane l comes from tile row row0 + spread_row(16t + 8(v/4) + 4g + v%4).
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 tr_operand_spread(const uint16_t* tile, int row0, int col0, int t, int lane) {
+  const int g = lane >> 5;
+  const uint16_t* p = tile + (row0 + 16 * t + 4 * ((lane & 15) >> 2) + g) * STRIDE + col0 +
+                      16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return bf16x8_from(lds_read_tr16(p), lds_read_tr16(p + 2 * STRIDE));
 }
 
 // Column of key k in a stored dS row: bits 2 and 3 of k swapped, so that the
@@ -214,9 +238,11 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   // past N lie past the end of the head's buffer and are dropped.
   const __amdgpu_buffer_rsrc_t dsr =
       make_rsrc(WRITE_DS ? dS + (size_t)bh * N * Nk : dS, WRITE_DS ? (uint32_t)N * Nk * 2 : 0u);
-  const uint32_t ds_off = WRITE_DS ? (uint32_t)(4 * g * Nk + ds_column(myk)) * 2 : 0u;
-  // element r of an accumulator is query row 8(r/4) + 4g + r%4 of the tile
-  auto ds_row = [&](int qt0, int r) { return (qt0 + 8 * (r >> 2) + (r & 3)) * Nk * 2; };
+  const uint32_t ds_off = WRITE_DS ? (uint32_t)(g * Nk + ds_column(myk)) * 2 : 0u;
+  // element r of an accumulator is query row spread_row(8(r/4) + 4g + r%4)
+  // of the tile, i.e. qrow(r) + g
+  auto qrow = [](int r) { return spread_row(8 * (r >> 2) + (r & 3)); };
+  auto ds_row = [&](int qt0, int r) { return (qt0 + qrow(r)) * Nk * 2; };
 
   // This lane's K row as the B operand of S = Q K^T (rows past N read as zero).
   bf16x8 kf[KSTEPS];
@@ -242,7 +268,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
 
   // Per-tile loads, straight into LDS: the Q and dO rows and the delta of
   // the tile's queries; wave 2 loads their LSE into a register and stores
-  // LSE * log2(e) at the end of the step.  Queries past N read as zero throughout, which
+  // LSE * log2(e) at the end of the step.  Slot x of the LSE and delta
+  // vectors holds query spread_row(x), the query of accumulator row x.  Queries past N read as zero throughout, which
   // makes their P = exp2(0) = 1 but their dO row, dP and delta zero, so they
   // add nothing to dV (P^T dO) or dK (dS^T Q with dS = P (dP - delta) = 0).
   // Load j of the 2 RI per tile (Q then dO) is issued by wave j % 4; lane l
@@ -256,6 +283,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     voff[u] = row < Q_TILE && col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
   }
   uint32_t lse_bits = 0;
+  const int srow = (lane & 32) | spread_row(l32);
   auto fetch = [&](int qt0, uint16_t* stage) {
 #pragma unroll
     for (int u = 0; u < NJ; ++u) {
@@ -265,8 +293,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         lds_load16(m ? grs : qrs, stage + m * L::TILE + jj * 512, voff[u] + (uint32_t)qt0 * D * 2);
       }
     }
-    if (wave == 2) lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + lane) * 4, 0, 0);
-    if (wave == 3) lds_load4(drs, stage + 2 * L::TILE + 128, (uint32_t)(qt0 + lane) * 4);
+    if (wave == 2) lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + srow) * 4, 0, 0);
+    if (wave == 3) lds_load4(drs, stage + 2 * L::TILE + 128, (uint32_t)(qt0 + srow) * 4);
   };
   auto put_lse = [&](uint16_t* stage) {
     if (wave == 2) reinterpret_cast<float*>(stage + 2 * L::TILE)[lane] = __uint_as_float(lse_bits) * kLog2e;
@@ -289,7 +317,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     if (i + 1 < ntiles) fetch(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
 
     if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
-      // S and dP: element r is query qt0 + 8(r/4) + 4g + r%4, key myk.  At
+      // S and dP: element r is query qt0 + qrow(r) + g, key myk.  At
       // d = 64 the dP accumulator starts from the tile's -delta values (the
       // workspace holds -delta), which saves a subtraction per element; at
       // d = 128 the extra live registers cost more than that saves, and the
@@ -306,8 +334,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        s = mfma32(row_operand<L::QS>(Qs, l32, ks, g), kf[ks], ks == 0 ? f32x16{} : s);
-        dp = mfma32(row_operand<L::QS>(Gs, l32, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
+        s = mfma32(row_operand<L::QS>(Qs, srow & 31, ks, g), kf[ks], ks == 0 ? f32x16{} : s);
+        dp = mfma32(row_operand<L::QS>(Gs, srow & 31, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
                     ks == 0 ? nd : dp);
       }
       // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
@@ -323,8 +351,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         }
         __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * STEPS, 0);
       }
-      // hidden when key > query, i.e. query offset 8(r/4) + r%4 < lim
-      const int lim = myk - qt0 - 4 * g;
+      // hidden when key > query, i.e. query offset qrow(r) + g < myk - qt0
+      const int lim = myk - qt0 - g;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 8 * a + 4 * g);
@@ -334,7 +362,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         for (int b = 0; b < 4; ++b) {
           const int r = 4 * a + b;
           float p = exp2_hw(__builtin_fmaf(s[r], c, -l4[b]));
-          if (CAUSAL && MASK && 8 * a + b < lim) p = 0.f;
+          if (CAUSAL && MASK && qrow(r) < lim) p = 0.f;
           s[r] = p;
           dp[r] = ND_INIT ? p * dp[r] : p * (dp[r] + d4[b]);
         }
@@ -356,8 +384,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvt[db] = mfma32(tr_operand<L::QS>(Gs, 0, 32 * db, t, lane), pb, dvt[db]);
-          dkt[db] = mfma32(tr_operand<L::QS>(Qs, 0, 32 * db, t, lane), dsb, dkt[db]);
+          dvt[db] = mfma32(tr_operand_spread<L::QS>(Gs, 0, 32 * db, t, lane), pb, dvt[db]);
+          dkt[db] = mfma32(tr_operand_spread<L::QS>(Qs, 0, 32 * db, t, lane), dsb, dkt[db]);
         }
       }
       // 4 transpose reads ahead, then one product per 2 reads.
@@ -525,6 +553,8 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
   wait_vmem();
   __syncthreads();
 
+  const int srow = spread_row(l32);
+  auto krow = [](int r) { return spread_row(8 * (r >> 2) + (r & 3)); };
   auto step = [&](int j, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int kv0 = j * K_TILE;
@@ -532,16 +562,17 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
     const uint16_t* Vs = Ks + L::K_ELEMS;
     if (j + 1 < ntiles) fetch(kv0 + K_TILE, smem + ((j + 1) & 1) * L::STAGE);
     if (!CAUSAL || !MASK || kv0 <= qw + 31) {
-      // hidden when key > myq, i.e. key offset 32kb + 8(r/4) + r%4 > lim
-      const int lim = myq - kv0 - 4 * g;
+      // hidden when key > myq, i.e. key offset 32kb + krow(r) > lim
+      const int lim = myq - kv0 - g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T and dP^T: element r is key kv0 + 32kb + 8(r/4) + 4g + r%4, query myq.
+        // S^T and dP^T: element r is key kv0 + 32kb + krow(r) + g, query
+        // myq, with the keys of each 32-row block in spread_row order.
         f32x16 s, dp;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-          s = mfma32(row_operand<L::KS>(Ks, kb * 32 + l32, ks, g), qf[ks], ks == 0 ? f32x16{} : s);
-          dp = mfma32(row_operand<L::VS>(Vs, kb * 32 + l32, ks, g), gf[ks], ks == 0 ? ndv : dp);
+          s = mfma32(row_operand<L::KS>(Ks, kb * 32 + srow, ks, g), qf[ks], ks == 0 ? f32x16{} : s);
+          dp = mfma32(row_operand<L::VS>(Vs, kb * 32 + srow, ks, g), gf[ks], ks == 0 ? ndv : dp);
         }
         // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
         // matrix-core instructions (mask 0x008), then 2 and 2 (measured 2-3%
@@ -559,7 +590,7 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = exp2_hw(__builtin_fmaf(s[r], c, -lse2));
-          if (CAUSAL && MASK && kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p = 0.f;
+          if (CAUSAL && MASK && kb * 32 + krow(r) > lim) p = 0.f;
           dp[r] = p * dp[r];
         }
 #pragma unroll
@@ -567,7 +598,7 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
           const bf16x8 dsb = acc_to_operand(dp, t);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            dqt[db] = mfma32(tr_operand<L::KS>(Ks, kb * 32, 32 * db, t, lane), dsb, dqt[db]);
+            dqt[db] = mfma32(tr_operand_spread<L::KS>(Ks, kb * 32, 32 * db, t, lane), dsb, dqt[db]);
         }
         // 4 transpose reads ahead, then one product per 2 reads.
         {
