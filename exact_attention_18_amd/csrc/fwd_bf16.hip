@@ -593,6 +593,13 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
   };
   using T = std::true_type;
   using F = std::false_type;
+  // Matrix phase k of the tiles that need the mask: when neither tile k
+  // nor tile k-1 holds a key this wave sees (both past its last query), the
+  // phase is skipped (the scores would go unused and P is zero); the
+  // barriers stay the same for every wave.
+  auto matrix_tail = [&](int k) {
+    if (k - 1 <= last_w) matrix(k, T{}, T{});
+  };
 
   pp_load<D>(rk, krs, 0, tid, PP_NT);   // K(0), whole tile
   pp_store<D, L::KS>(rk, kslot(0), tid, PP_NT);
@@ -619,14 +626,14 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
       pp_sync();
     }
     for (; k < ntiles; ++k) {
-      matrix(k, T{}, T{});
+      matrix_tail(k);
       pp_sync();
       softmax(k, T{});
       store(k);
       fetch(k + 1);
       pp_sync();
     }
-    matrix(ntiles, F{}, T{});
+    if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
     pp_sync();
     pp_sync();
   } else {
@@ -649,12 +656,12 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
       store(k);
       fetch(k + 1);
       pp_sync();
-      matrix(k, T{}, T{});
+      matrix_tail(k);
       pp_sync();
     }
     if (ntiles - 1 < first_mask_w) softmax(ntiles - 1, F{}); else softmax(ntiles - 1, T{});
     pp_sync();
-    matrix(ntiles, F{}, T{});
+    if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
     pp_sync();
   }
 
