@@ -252,12 +252,10 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     for (int ks = 0; ks < KSTEPS; ++ks)
       kf[ks] = bf16x8_from(buf_load16(krs, (uint32_t)((myk * D + ks * 16 + 8 * g) * 2)));
   }
-  // The workgroup's V rows, staged once (B operand of dP = dO V^T).
-  {
-    Rows<KV_BLK, D> vrows;
-    vrows.load(make_rsrc(V + base, head_bytes), k0, tid);
-    vrows.template store<L::VS>(Vs, tid);
-  }
+  // The workgroup's V rows, staged once (B operand of dP = dO V^T): loaded
+  // here, stored to LDS after the first tile's loads are issued.
+  Rows<KV_BLK, D> vrows;
+  vrows.load(make_rsrc(V + base, head_bytes), k0, tid);
 
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -301,6 +299,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   };
 
   fetch(qstart, smem + L::V_ELEMS);
+  vrows.template store<L::VS>(Vs, tid);
   put_lse(smem + L::V_ELEMS);
   wait_vmem();
   __syncthreads();
@@ -476,6 +475,31 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
     }
   }
   const float lse2 = myq < N ? LSE[(size_t)bh * N + myq] * kLog2e : INFINITY;
+  // K and V tiles come by direct HBM -> LDS loads: load j of a tile pair (K
+  // loads first, then V) is issued by wave j % 4, and lane l of a load fills
+  // the 16-byte chunk 64 (its index within the tile) + l of the padded rows;
+  // lanes on a row's padding get an offset past the buffer (zeros).
+  constexpr int NL = L::KLOADS + L::VLOADS, PW = (NL + 3) / 4;
+  uint32_t voff[PW];
+#pragma unroll
+  for (int u = 0; u < PW; ++u) {
+    const int j = wave + 4 * u;
+    const bool isv = j >= L::KLOADS;
+    const int cpr = isv ? L::VCPR : L::KCPR;
+    const int p = 64 * (isv ? j - L::KLOADS : j) + lane, row = p / cpr, col = p % cpr;
+    voff[u] = col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
+  }
+  auto fetch = [&](int kv0, uint16_t* stage) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int j = wave + 4 * u;
+      if (j < L::KLOADS)
+        lds_load16(krs, stage + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
+      else if (j < NL)
+        lds_load16(vrs, stage + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
+    }
+  };
+  fetch(0, smem);   // the first tiles load while -delta is computed
   // -delta of this lane's query (the workspace holds -delta): the dP^T
   // accumulators start from it
   float ndl;
@@ -525,31 +549,6 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
 
   const int kv_end = CAUSAL ? min(N, q0 + Q_BLK) : N;
   const int ntiles = (kv_end + K_TILE - 1) / K_TILE;
-  // K and V tiles come by direct HBM -> LDS loads: load j of a tile pair (K
-  // loads first, then V) is issued by wave j % 4, and lane l of a load fills
-  // the 16-byte chunk 64 (its index within the tile) + l of the padded rows;
-  // lanes on a row's padding get an offset past the buffer (zeros).
-  constexpr int NL = L::KLOADS + L::VLOADS, PW = (NL + 3) / 4;
-  uint32_t voff[PW];
-#pragma unroll
-  for (int u = 0; u < PW; ++u) {
-    const int j = wave + 4 * u;
-    const bool isv = j >= L::KLOADS;
-    const int cpr = isv ? L::VCPR : L::KCPR;
-    const int p = 64 * (isv ? j - L::KLOADS : j) + lane, row = p / cpr, col = p % cpr;
-    voff[u] = col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
-  }
-  auto fetch = [&](int kv0, uint16_t* stage) {
-#pragma unroll
-    for (int u = 0; u < PW; ++u) {
-      const int j = wave + 4 * u;
-      if (j < L::KLOADS)
-        lds_load16(krs, stage + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
-      else if (j < NL)
-        lds_load16(vrs, stage + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
-    }
-  };
-  fetch(0, smem);
   wait_vmem();
   __syncthreads();
 
