@@ -601,9 +601,14 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
     if (k - 1 <= last_w) matrix(k, T{}, T{});
   };
 
-  pp_load<D>(rk, krs, 0, tid, PP_NT);   // K(0), whole tile
-  pp_store<D, L::KS>(rk, kslot(0), tid, PP_NT);
-  fetch(0);
+  {
+    // K(0), whole tile, in its own registers, so that this group's halves of
+    // K(1) and V(0) are in flight at the same time
+    u32x4 rk0[L::CPT];
+    pp_load<D>(rk0, krs, 0, tid, PP_NT);
+    fetch(0);
+    pp_store<D, L::KS>(rk0, kslot(0), tid, PP_NT);
+  }
   pp_sync();
 
   // Pairs 1 .. ntiles-1 run the full matrix phase; the pairs whose softmax
