@@ -17,6 +17,14 @@ with the largest average duration is reported with its roofline:
 achieved = its algorithmic FLOPs per launch / its average duration, against
 the MI355X dense bf16 matrix-core peak.
 
+Timing series (page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の
+実践的エンジニアリング", section 「推論レイテンシとスループットの測定方法」: CUDA events
+around repeated launches after warm-up): the step and every secondary
+workload are also launched SERIES_N times, each launch bracketed by its own
+pair of HIP events, and reported as the median and the minimum; a second
+series writes a 512 MiB scratch buffer before every launch, which evicts the
+L2 caches and the MALL, so that no input starts out on chip.
+
 cpu_baseline: the fp64 oracle (materialising S and P) timed on the host on
 the first whole heads of the same workload, forward+backward, for about
 ``--cpu-seconds`` seconds.
@@ -42,7 +50,12 @@ PEAK_FP8_TFLOPS = 5033.2   # dense FP8 matrix cores, twice the bf16 rate
 DEFAULT_WORKLOAD = "bf16_b8h16n2048d128_causal_fwdbwd"
 CLOCK_WARMUP_S = 1.0   # untimed work before the timed steps (clock ramp-up)
 CLOCK_REWARM_S = 0.3   # untimed burst before each secondary measurement
-HEADLINE_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal", "bf16_b1h16n16384d128"]
+HEADLINE_FWD = ["bf16_b16h32n1024d64", "bf16_b16h32n1024d64_causal", "bf16_b4h16n4096d128_causal_x0.5",
+                "bf16_b1h16n16384d128_causal", "bf16_b1h16n16384d128"]
+FP8_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal", "bf16_b1h16n16384d128"]
+EXTRA_BWD = ["bf16_b16h32n1024d64_causal_fwdbwd"]
+SERIES_N = 20          # launches per timing series
+FLUSH_MIB = 512        # scratch written before each launch of the flushed series
 
 
 def _products(w, n):
@@ -65,10 +78,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    counter summary, or None if there is none for the current sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+def _profile_fields(name: str):
+    """Fields of a committed counter summary profiles/<name>.txt, or None if
+    there is none or it was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", name + ".txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -79,10 +92,33 @@ def measured_traffic(kernel: str, workload: str):
                 fields[key.strip()] = val.strip()
     if fields.get("source_digest") != kernel_source_digest():
         return None
+    return fields
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    FETCH_SIZE / WRITE_SIZE summary, or None."""
+    fields = _profile_fields(f"traffic_{kernel}_{workload}")
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields["traffic_bytes_per_launch"]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def measured_mfma(kernel: str, workload: str):
+    """Matrix-core counters of `kernel` on `workload` from the committed
+    summary (SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES against
+    SQ_BUSY_CU_CYCLES, GRBM_GUI_ACTIVE), or None."""
+    fields = _profile_fields(f"mfma_{kernel}_{workload}")
+    if not fields:
+        return None
+    out = {}
+    for key in ("counter_flop_per_launch", "mfma_busy_frac", "gpu_clock_ghz", "kernel_us"):
+        try:
+            out[key] = float(fields[key])
+        except (KeyError, ValueError):
+            pass
+    return out or None
 
 
 def copy_calibration(dev, mib: int, reps: int):
@@ -159,42 +195,51 @@ def main():
     import fa_inputs as fi
 
     fa._lib.load()  # raises if the HIP library is missing
-    w = fi.WORKLOADS[args.workload]
+    w = fi.WORKLOADS.get(args.workload) or fi.EXTRA_WORKLOADS[args.workload]
     if w.dtype != "bf16":
         raise SystemExit("bench.py times the bf16 path")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
 
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x = fi.make_inputs(w, with_grad=True)
-    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
-    B, H, N, d, causal, scale = w.B, w.H, w.N, w.d, int(w.causal), w.scale
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = fa.fa_backward_workspace_size(B, H, N, d)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-    P = {n: t.data_ptr() for n, t in dict(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws).items()}
+    def checked(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {fa.fa_status_string(st)}")
 
-    kernels = [
-        ("fwd", lambda: fa.fa_forward(P["q"], P["k"], P["v"], P["o"], P["lse"], B, H, N, d, causal, scale, sp),
-         _products(w, 2)),
-    ]
-    if w.backward:
-        # The backward as fa_backward runs it at this size: dQ (computing
-        # -delta of its queries on the way), then dK/dV.
-        kernels += [
-            ("bwd_dq", lambda: fa.fa_backward_dq_delta(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"],
-                                                       B, H, N, d, causal, scale, P["ws"], ws_bytes, sp),
-             _products(w, 1)),
-            ("bwd_dkdv", lambda: fa.fa_backward_dkdv(P["q"], P["k"], P["v"], P["lse"], P["do"], P["dk"], P["dv"],
-                                                     B, H, N, d, causal, scale, P["ws"], ws_bytes, sp),
-             _products(w, 4)),
-        ]
+    def step_kernels(wl, with_backward):
+        """Device tensors of a workload and its kernels as the library runs
+        them: forward, then (large grids) dQ computing -delta, then dK/dV."""
+        x = fi.make_inputs(wl, with_grad=with_backward)
+        t = {n: to_dev(a) for n, a in x.items()}
+        B_, H_, N_, d_ = wl.B, wl.H, wl.N, wl.d
+        c_, s_ = int(wl.causal), wl.scale
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((B_, H_, N_), dtype=torch.float32, device=dev)
+        ks = [("fwd", lambda: fa.fa_forward(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                            t["o"].data_ptr(), t["lse"].data_ptr(), B_, H_, N_, d_, c_, s_, sp),
+               _products(wl, 2))]
+        if with_backward:
+            for n in ("dq", "dk", "dv"):
+                t[n] = torch.empty_like(t["q"])
+            nb = fa.fa_backward_workspace_size(B_, H_, N_, d_)
+            t["ws"] = torch.empty(nb, dtype=torch.uint8, device=dev)
+            P_ = {n: v.data_ptr() for n, v in t.items()}
+            ks += [
+                ("bwd_dq", lambda: fa.fa_backward_dq_delta(P_["q"], P_["k"], P_["v"], P_["o"], P_["lse"], P_["do"],
+                                                           P_["dq"], B_, H_, N_, d_, c_, s_, P_["ws"], nb, sp),
+                 _products(wl, 1)),
+                ("bwd_dkdv", lambda: fa.fa_backward_dkdv(P_["q"], P_["k"], P_["v"], P_["lse"], P_["do"], P_["dk"],
+                                                         P_["dv"], B_, H_, N_, d_, c_, s_, P_["ws"], nb, sp),
+                 _products(wl, 4)),
+            ]
+        return t, ks
+
+    tensors, kernels = step_kernels(w, w.backward)
+    B, H, N, d, causal, scale = w.B, w.H, w.N, w.d, int(w.causal), w.scale
     step_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
 
     def clock_warm(fn, seconds=CLOCK_WARMUP_S):
@@ -206,15 +251,16 @@ def main():
                 fn()
             torch.cuda.synchronize()
 
-    def run_step(evs=None):
-        for i, (name, fn, _) in enumerate(kernels):
+    def run_kernels(ks, evs=None):
+        for i, (name, fn, _) in enumerate(ks):
             if evs is not None:
                 evs[i][0].record(stream)
-            st = fn()
-            if st != 0:
-                raise RuntimeError(f"{name}: {fa.fa_status_string(st)}")
+            checked(fn(), name)
             if evs is not None:
                 evs[i][1].record(stream)
+
+    def run_step(evs=None):
+        run_kernels(kernels, evs)
 
     # The GPU runs at lower clocks for roughly its first second of work, so
     # the step runs untimed for CLOCK_WARMUP_S before the W warm-up steps.
@@ -243,40 +289,77 @@ def main():
                         "tflops": round(f / (per_kernel_ms[n] * 1e-3) / 1e12, 1) if f else None}
                     for n, _, f in kernels}
 
-    def time_launches(fn, n=10, warm=3):
-        """Mean HIP-event time (ms) of ``fn`` launched ``n`` times on ``stream``,
-        after a short untimed burst that brings the clocks back up."""
+    flush_buf = torch.empty(FLUSH_MIB * 2**20, dtype=torch.uint8, device=dev)
+    flush_val = [0]
+
+    def flush():
+        flush_val[0] = (flush_val[0] + 1) & 0xFF
+        flush_buf.fill_(flush_val[0])
+
+    def series(fn, flushed, n=SERIES_N, warm=3):
+        """HIP-event times (ms) of ``fn`` launched ``n`` times on ``stream``,
+        each launch bracketed by its own events (after a short untimed burst
+        that brings the clocks back up); ``flushed`` writes the scratch buffer
+        before every launch.  Returns median, minimum and mean."""
         clock_warm(fn, CLOCK_REWARM_S)
         for _ in range(warm):
             fn()
         evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for a, b_ in evs_:
+            if flushed:
+                flush()
             a.record(stream)
             fn()
             b_.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b_) for a, b_ in evs_]))
+        t = np.array([a.elapsed_time(b_) for a, b_ in evs_])
+        return {"median_ms": round(float(np.median(t)), 4), "min_ms": round(float(t.min()), 4),
+                "mean_ms": round(float(t.mean()), 4), "n": n}
 
-    def checked(st, what):
-        if st != 0:
-            raise RuntimeError(f"{what}: {fa.fa_status_string(st)}")
+    def both_series(fn, flops):
+        out = {}
+        for key, fl in (("warm", False), ("flushed", True)):
+            sr = series(fn, fl)
+            sr["tflops_median"] = round(flops / (sr["median_ms"] * 1e-3) / 1e12, 1)
+            sr["frac_of_peak_median"] = round(sr["tflops_median"] / PEAK_BF16_TFLOPS, 4)
+            out[key] = sr
+        return out
+
+    step_series = both_series(run_step, step_flops)
+    backward_series = None
+    if w.backward:
+        backward_series = both_series(lambda: checked(fa.fa_backward(
+            *(tensors[n].data_ptr() for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")),
+            B, H, N, d, causal, scale, tensors["ws"].data_ptr(), tensors["ws"].numel(), sp), "backward"),
+            w.bwd_flops())
 
     headline = []
+    extra_backward = []
     block_sparse = []
     if not args.no_headline:
         for name in HEADLINE_FWD:
             hw = fi.WORKLOADS[name]
-            hx = fi.make_inputs(hw, with_grad=False)
-            hq, hk, hv = (to_dev(hx[n]) for n in ("q", "k", "v"))
-            ho = torch.empty_like(hq)
-            hl = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=dev)
-            hms = time_launches(lambda: checked(fa.fa_forward(
-                hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), ho.data_ptr(), hl.data_ptr(),
-                hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale, sp), "fwd"))
-            tf = hw.fwd_flops() / (hms * 1e-3) / 1e12
-            headline.append({"workload": name, "kernel": "fwd", "ms": round(hms, 4), "tflops": round(tf, 1),
-                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-            del hq, hk, hv, ho, hl
+            ht, hk = step_kernels(hw, False)
+            sr = both_series(lambda: checked(hk[0][1](), "fwd"), hw.fwd_flops())
+            tf = sr["warm"]["tflops_median"]
+            headline.append({"workload": name, "kernel": "fwd", "ms": sr["warm"]["median_ms"], "tflops": tf,
+                             "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "series": sr})
+            del ht, hk
+
+        # d = 64 forward + backward: the step's kernels at that shape, and
+        # fa_backward as a whole.
+        for name in EXTRA_BWD:
+            ew = fi.EXTRA_WORKLOADS[name]
+            et, ek = step_kernels(ew, True)
+            run_kernels(ek)
+            torch.cuda.synchronize()
+            ebw = both_series(lambda: checked(fa.fa_backward(
+                *(et[n].data_ptr() for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")),
+                ew.B, ew.H, ew.N, ew.d, int(ew.causal), ew.scale, et["ws"].data_ptr(), et["ws"].numel(), sp),
+                "backward"), ew.bwd_flops())
+            estep = both_series(lambda: run_kernels(ek), ew.fwd_flops() + ew.bwd_flops())
+            extra_backward.append({"workload": name, "fa_backward": ebw, "step": estep})
+            del et, ek
 
         # Block-sparse forward: FLOPs counted on the visible (query, key)
         # pairs only; the dense forward at the same shape is timed beside it.
@@ -290,14 +373,14 @@ def main():
             args_ = (bq.data_ptr(), bk.data_ptr(), bv.data_ptr(), bo.data_ptr(), bl.data_ptr())
             bsw = fa.fa_block_sparse_workspace_size(bw.B, bw.H, bw.N, bw.d)
             bws = torch.empty(bsw, dtype=torch.uint8, device=dev)
-            sms = time_launches(lambda: checked(fa.fa_forward_block_sparse(
+            sms = series(lambda: checked(fa.fa_forward_block_sparse(
                 *args_, bm.data_ptr(), bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, bws.data_ptr(), bsw, sp),
-                "block_sparse"))
-            sms_one = time_launches(lambda: checked(fa.fa_forward_block_sparse(
+                "block_sparse"), False)["median_ms"]
+            sms_one = series(lambda: checked(fa.fa_forward_block_sparse(
                 *args_, bm.data_ptr(), bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, 0, 0, sp),
-                "block_sparse_one_pass"))
-            dms = time_launches(lambda: checked(fa.fa_forward(
-                *args_, bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, sp), "fwd"))
+                "block_sparse_one_pass"), False)["median_ms"]
+            dms = series(lambda: checked(fa.fa_forward(
+                *args_, bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, sp), "fwd"), False)["median_ms"]
             tf = sw.fwd_flops() / (sms * 1e-3) / 1e12
             block_sparse.append({"workload": name, "kernel": "fwd_block_sparse",
                                  "density": round(float(sw.mask().mean()), 4), "ms": round(sms, 4),
@@ -312,7 +395,7 @@ def main():
     fp8 = []
     if not args.no_headline:
         signs = torch.from_numpy(fi.random_signs(0, 128)).to(dev)
-        for name in HEADLINE_FWD:
+        for name in FP8_FWD:
             hw = fi.WORKLOADS[name]
             hx = fi.make_inputs(hw, with_grad=False)
             hq, hk, hv = (to_dev(hx[n]) for n in ("q", "k", "v"))
@@ -320,12 +403,12 @@ def main():
             hl = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=dev)
             nb = fa.fa_fp8_buffer_size(hw.B, hw.H, hw.N, hw.d)
             hb = torch.empty(nb, dtype=torch.uint8, device=dev)
-            pms = time_launches(lambda: checked(fa.fa_fp8_prepare(
+            pms = series(lambda: checked(fa.fa_fp8_prepare(
                 hq.data_ptr(), hk.data_ptr(), hv.data_ptr(), signs.data_ptr(), hw.B, hw.H, hw.N, hw.d,
-                hb.data_ptr(), nb, sp), "fp8_prepare"))
-            fms = time_launches(lambda: checked(fa.fa_forward_fp8_prepared(
+                hb.data_ptr(), nb, sp), "fp8_prepare"), False)["median_ms"]
+            fms = series(lambda: checked(fa.fa_forward_fp8_prepared(
                 hb.data_ptr(), nb, ho.data_ptr(), hl.data_ptr(), hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale,
-                1, sp), "fp8_forward"))
+                1, sp), "fp8_forward"), False)["median_ms"]
             tf = hw.fwd_flops() / (fms * 1e-3) / 1e12
             fp8.append({"workload": name, "kernel": "fwd_fp8", "prepare_ms": round(pms, 4), "ms": round(fms, 4),
                         "tflops": round(tf, 1), "peak_fp8": PEAK_FP8_TFLOPS,
@@ -344,36 +427,18 @@ def main():
             dl_ = torch.empty((dw.B, dw.H, dw.Nq), dtype=torch.float32, device=dev)
             dws_bytes = fa.fa_decode_workspace_size(dw.B, dw.H, dw.Nq, dw.Nk, dw.d)
             dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
-            dms = time_launches(lambda: checked(fa.fa_decode(
+            dsr = series(lambda: checked(fa.fa_decode(
                 dq_.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), do_.data_ptr(), dl_.data_ptr(), dw.B, dw.H,
-                dw.Nq, dw.Nk, dw.d, int(dw.causal), dw.scale, dws.data_ptr(), dws_bytes, sp), "decode"), n=20)
+                dw.Nq, dw.Nk, dw.d, int(dw.causal), dw.scale, dws.data_ptr(), dws_bytes, sp), "decode"), True)
+            dms = dsr["median_ms"]
             gbs = dw.hbm_bytes() / (dms * 1e-3) / 1e9
-            decode.append({"workload": name, "entry": "fa_decode", "ms": round(dms, 4),
+            decode.append({"workload": name, "entry": "fa_decode", "ms": round(dms, 4), "flushed": True,
                            "algorithmic_bytes": dw.hbm_bytes(), "GB_per_s": round(gbs, 1),
                            "hbm_peak_GB_per_s": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                            "tflops": round(dw.flops() / (dms * 1e-3) / 1e12, 2)})
             del dq_, dk_, dv_, do_, dl_, dws
 
-    # Backward with a stored dS (fa_backward_stored_ds, O(N^2) workspace) on
-    # the step's own tensors, beside fa_backward on the same tensors: both
-    # whole backward passes (row-dot pre-pass included), same FLOP count.
-    stored_ds = []
-    if w.backward and not args.no_headline:
-        sws_bytes = fa.fa_backward_stored_ds_workspace_size(B, H, N, d)
-        if sws_bytes:
-            sws = torch.empty(sws_bytes, dtype=torch.uint8, device=dev)
-            args_b = (P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["dq"], P["dk"], P["dv"], B, H, N, d,
-                      causal, scale)
-            sms_ = time_launches(lambda: checked(fa.fa_backward_stored_ds(*args_b, sws.data_ptr(), sws_bytes, sp),
-                                                 "backward_stored_ds"))
-            bms_ = time_launches(lambda: checked(fa.fa_backward(*args_b, P["ws"], ws_bytes, sp), "backward"))
-            bf = w.bwd_flops()
-            stored_ds.append({"workload": w.name, "entry": "fa_backward_stored_ds", "ms": round(sms_, 4),
-                              "tflops": round(bf / (sms_ * 1e-3) / 1e12, 1), "workspace_MiB": round(sws_bytes / 2**20),
-                              "fa_backward_ms": round(bms_, 4),
-                              "fa_backward_tflops": round(bf / (bms_ * 1e-3) / 1e12, 1)})
-            del sws
-
+    del flush_buf
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
 
@@ -382,6 +447,22 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+    mfma = measured_mfma(dom[0], w.name)
+    roofline = {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom[0], w.name),
+                "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)}
+    if mfma:
+        # the matrix-core work the counters saw (recomputed products
+        # included) over this run's launch time, and the busy fraction
+        if "counter_flop_per_launch" in mfma:
+            roofline["counter_tflops"] = round(mfma["counter_flop_per_launch"] / (dom_ms * 1e-3) / 1e12, 1)
+            roofline["counter_frac"] = round(roofline["counter_tflops"] / PEAK_BF16_TFLOPS, 4)
+        if "mfma_busy_frac" in mfma:
+            roofline["mfma_busy_frac"] = mfma["mfma_busy_frac"]
+        if "gpu_clock_ghz" in mfma:
+            roofline["gpu_clock_ghz"] = mfma["gpu_clock_ghz"]
     out = {
         "metric": "attention fwd/bwd TFLOPs/s (bf16, d=64/128, causal) + % of MFMA bf16 peak",
         "value": round(value, 2),
@@ -400,21 +481,18 @@ def main():
                    "step_gflop": round(step_flops / 1e9, 2), "parallelism": "single GPU",
                    "clock_warmup_s": CLOCK_WARMUP_S,
                    "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4)},
-        "roofline": {"bound": "mfma", "kernel": dom[0], "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(dom[0], w.name),
-                     "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)},
+        "roofline": roofline,
         "kernels": kernel_table,
+        "series": {"launches": SERIES_N, "flush_MiB": FLUSH_MIB, "step": step_series,
+                   "fa_backward": backward_series},
         "headline_forward": headline,
+        "backward_d64": extra_backward,
         "block_sparse_forward": block_sparse,
         "decode": decode,
         "fp8_forward": fp8,
-        "backward_stored_ds": stored_ds,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-
 
 if __name__ == "__main__":
     main()

@@ -1,6 +1,7 @@
 // C ABI entry points (declared in include/fa.h): argument checks on the
 // host, then dispatch to the launchers.  No allocation, no global state.
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 #include "fa.h"
@@ -59,7 +60,23 @@ int check_buffers(const Span* ins, const void* const* in_ptrs, int n_in, const S
   return FA_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+// Status of a launch.  With FA_SYNC_DEBUG=1 in the environment the stream is
+// also synchronised after every entry point and any error it reports
+// (including a fault in the kernels just launched) is returned as
+// FA_ERR_HIP; this serialises the caller's work and is meant for debugging.
+bool sync_debug() {
+  const char* v = getenv("FA_SYNC_DEBUG");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+int hip_status(hipError_t e, void* stream) {
+  if (e != hipSuccess) return FA_ERR_HIP;
+  if (sync_debug()) {
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return FA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
 
 template <typename T>
 int forward_impl(const T* q, const T* k, const T* v, T* o, float* lse, int B, int H, int N, int d,
@@ -76,9 +93,9 @@ int forward_impl(const T* q, const T* k, const T* v, T* o, float* lse, int B, in
   if (st != FA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if constexpr (sizeof(T) == 2)
-    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s), stream);
   else
-    return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+    return hip_status(fa::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s), stream);
 }
 
 template <typename T>
@@ -101,10 +118,10 @@ int backward_impl(const T* q, const T* k, const T* v, const T* o, const float* l
   float* delta = static_cast<float*>(workspace);
   if constexpr (sizeof(T) == 2)
     return hip_status(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, B * H, N, d, causal != 0,
-                                          scale, delta, s));
+                                          scale, delta, s), stream);
   else
     return hip_status(fa::launch_bwd_f32(q, k, v, o, lse, dO, dq, dk, dv, B * H, N, d, causal != 0,
-                                         scale, delta, s));
+                                         scale, delta, s), stream);
 }
 
 // Shared checks of the bf16 backward stages.  `ws_written` says whether the
@@ -152,7 +169,7 @@ int fa_backward_preprocess(const void* o, const void* dO, int B, int H, int N, i
   if (st != FA_OK) return st;
   return hip_status(fa::launch_rowdot_bf16(static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
                                            static_cast<float*>(workspace), (long long)B * H * N, d,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dk,
@@ -166,7 +183,7 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const float* l
   return hip_status(fa::launch_bwd_dkdv_bf16(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), lse,
       static_cast<const uint16_t*>(dO), static_cast<const float*>(workspace), static_cast<uint16_t*>(dk),
-      static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+      static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, void* dq,
@@ -180,7 +197,7 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const float* lse
   return hip_status(fa::launch_bwd_dq_bf16(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), lse,
       static_cast<const uint16_t*>(dO), static_cast<const float*>(workspace), static_cast<uint16_t*>(dq), B * H,
-      N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+      N, d, causal != 0, scale, static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -194,7 +211,7 @@ int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void
   return hip_status(fa::launch_bwd_dq_delta_bf16(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<float*>(workspace),
-      static_cast<uint16_t*>(dq), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)));
+      static_cast<uint16_t*>(dq), B * H, N, d, causal != 0, scale, static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -253,7 +270,7 @@ int fa_forward_block_sparse(const void* q, const void* k, const void* v, void* o
   return hip_status(fa::launch_fwd_bf16_block_sparse(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<uint16_t*>(o), lse, block_mask, B * H, N, d, causal != 0, scale, workspace,
-      static_cast<hipStream_t>(stream)));
+      static_cast<hipStream_t>(stream)), stream);
 }
 
 size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
@@ -286,7 +303,7 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
   return hip_status(fa::launch_decode_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
                                            B * H, Nq, Nk, d, causal != 0, scale, workspace,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream)), stream);
 }
 
 size_t fa_fp8_buffer_size(int B, int H, int N, int d) {
@@ -313,7 +330,7 @@ int fa_fp8_prepare(const void* q, const void* k, const void* v, const float* sig
   if (st != FA_OK) return st;
   return hip_status(fa::launch_fp8_prepare(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                            static_cast<const uint16_t*>(v), signs, B * H, N, buf,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_forward_fp8_prepared(const void* buf, size_t buf_bytes, void* o, float* lse, int B, int H, int N, int d,
@@ -332,7 +349,7 @@ int fa_forward_fp8_prepared(const void* buf, size_t buf_bytes, void* o, float* l
   st = check_buffers(ins, inp, 1, outs, outp, 2);
   if (st != FA_OK) return st;
   return hip_status(fa::launch_fwd_fp8(buf, static_cast<uint16_t*>(o), lse, B * H, N, causal != 0, scale,
-                                       rotated != 0, static_cast<hipStream_t>(stream)));
+                                       rotated != 0, static_cast<hipStream_t>(stream)), stream);
 }
 
 int fa_forward_fp8(const void* q, const void* k, const void* v, const float* signs, void* o, float* lse, int B,
@@ -355,7 +372,7 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, const float* sig
                                               static_cast<const uint16_t*>(v), signs, B * H, N, buf, s);
   if (e != hipSuccess) return FA_ERR_HIP;
   return hip_status(fa::launch_fwd_fp8(buf, static_cast<uint16_t*>(o), lse, B * H, N, causal != 0, scale,
-                                       signs != nullptr, s));
+                                       signs != nullptr, s), stream);
 }
 
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
@@ -371,41 +388,6 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                        static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d, causal,
                        scale, workspace, workspace_bytes, stream, true);
-}
-
-size_t fa_backward_stored_ds_workspace_size(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  const long long nk = (N + 127LL) / 128 * 128;
-  if ((N + 128LL) * nk * 2 >= (1LL << 31)) return 0;
-  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
-  const unsigned long long ds = bh * (unsigned long long)N * (unsigned long long)nk * 2ULL;
-  if (ds / 2ULL / (unsigned long long)nk / (unsigned long long)N != bh || ds > (1ULL << 50)) return 0;
-  return fa_backward_workspace_size(B, H, N, d) + (size_t)ds;
-}
-
-int fa_backward_stored_ds(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                          const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                          int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  size_t elems = 0;
-  int st = check_common(B, H, N, d, causal, scale, true, &elems);
-  if (st != FA_OK) return st;
-  const size_t need = fa_backward_stored_ds_workspace_size(B, H, N, d);
-  if (need == 0) return FA_ERR_UNSUPPORTED;
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
-  const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
-  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(lse, lb), span(dO, tb)};
-  const void* inp[6] = {q, k, v, o, lse, dO};
-  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
-  const void* outp[4] = {dq, dk, dv, workspace};
-  st = check_buffers(ins, inp, 6, outs, outp, 4);
-  if (st != FA_OK) return st;
-  float* delta = static_cast<float*>(workspace);
-  uint16_t* ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + fa_backward_workspace_size(B, H, N, d));
-  return hip_status(fa::launch_bwd_stored_ds_bf16(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, delta, ds,
-      static_cast<hipStream_t>(stream)));
 }
 
 int fa_backward_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,

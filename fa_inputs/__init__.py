@@ -125,6 +125,15 @@ WORKLOADS = {
         "bf16_b8h16n2048d128_causal_fwdbwd", "bf16", 8, 16, 2048, 128, True, backward=True),
 }
 
+# Secondary problems: the d = 64 shape above with a backward pass as well
+# (Q, K, V, dO drawn in that order), so that both head dimensions have a
+# measured backward.
+EXTRA_WORKLOADS = {
+    "bf16_b16h32n1024d64_causal_fwdbwd": Workload(
+        "bf16_b16h32n1024d64_causal_fwdbwd", "bf16", 16, 32, 1024, 64, True, backward=True),
+}
+__all__.append("EXTRA_WORKLOADS")
+
 
 def make_inputs(w: Workload, with_grad: bool | None = None):
     """Inputs of a workload as numpy arrays.

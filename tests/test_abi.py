@@ -285,61 +285,6 @@ def test_block_sparse_workspace(lib):
     assert sparse(lib, ws=ptr(3, 16), ws_bytes=need) == INVALID         # inside o
 
 
-# ---- backward with stored dS
-
-def bwd_ds(lib, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None, ws_bytes=None):
-    p = ptrs or [ptr(i) for i in range(10)]
-    if ws_bytes is None:
-        ws_bytes = lib.fa_backward_stored_ds_workspace_size(B, H, N, d)
-    return lib.fa_backward_stored_ds(*p[:9], B, H, N, d, causal, scale, p[9], ws_bytes, None)
-
-
-def test_stored_ds_workspace_size(lib):
-    # the fa_backward workspace, then B*H*N*Nk bf16 with Nk = N rounded up to 128
-    assert lib.fa_backward_stored_ds_workspace_size(8, 16, 2048, 128) == 8 * 16 * 2048 * 4 + 8 * 16 * 2048 * 2048 * 2
-    assert lib.fa_backward_stored_ds_workspace_size(1, 2, 33, 64) == 512 + 2 * 33 * 128 * 2  # delta: 66 rows, 264 -> 512 B
-    assert lib.fa_backward_stored_ds_workspace_size(0, 1, 8, 64) == 0
-    assert lib.fa_backward_stored_ds_workspace_size(1, 1, -1, 64) == 0
-    # one head's dS must stay below 2 GiB: (N + 128) * Nk * 2 < 2^31
-    assert lib.fa_backward_stored_ds_workspace_size(1, 1, 32000, 128) > 0
-    assert lib.fa_backward_stored_ds_workspace_size(1, 1, 32736, 128) == 0
-
-
-@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(causal=2), dict(scale=-1.0), dict(scale=math.nan)])
-def test_stored_ds_rejects_bad_sizes(lib, kw):
-    assert bwd_ds(lib, ws_bytes=1 << 20, **kw) == INVALID
-
-
-@pytest.mark.parametrize("d", [16, 96, 256])
-def test_stored_ds_rejects_unsupported_head_dim(lib, d):
-    assert bwd_ds(lib, d=d, ws_bytes=1 << 20) == UNSUP
-
-
-def test_stored_ds_rejects_huge_n(lib):
-    assert bwd_ds(lib, N=40000, ws_bytes=1 << 40) == UNSUP
-
-
-@pytest.mark.parametrize("which", range(10))
-def test_stored_ds_rejects_null_and_misaligned(lib, which):
-    p = [ptr(i) for i in range(10)]
-    p[which] = None
-    assert bwd_ds(lib, ptrs=p) == INVALID
-    p = [ptr(i) for i in range(10)]
-    p[which] = ptr(which, 4)
-    assert bwd_ds(lib, ptrs=p) == INVALID
-
-
-def test_stored_ds_rejects_overlaps_and_small_workspace(lib):
-    base = [ptr(i) for i in range(10)]
-    p = list(base)
-    p[9] = base[8] + 64   # workspace starts inside dv
-    assert bwd_ds(lib, ptrs=p) == INVALID
-    need = lib.fa_backward_stored_ds_workspace_size(1, 1, 8, 64)
-    assert bwd_ds(lib, ws_bytes=need - 1) == INVALID
-    # the workspace must hold the dS^T part too, not only fa_backward's part
-    assert bwd_ds(lib, ws_bytes=lib.fa_backward_workspace_size(1, 1, 8, 64)) == INVALID
-
-
 # The stages of fa_backward: name -> (number of leading pointer arguments,
 # whether causal and scale follow the sizes, indices of the outputs among
 # those pointers).  The workspace pointer comes after the sizes.
