@@ -42,6 +42,7 @@ __all__ = [
     "make_decode_inputs",
     "random_signs",
     "with_outliers",
+    "with_channel_outliers",
 ]
 
 
@@ -299,4 +300,20 @@ def with_outliers(x: np.ndarray, seed: int, frac: float = 0.001, factor: float =
     out = np.array(x, dtype=np.float32, copy=True)
     hit = rng.random(out.shape) < frac
     out[hit] *= np.float32(factor)
+    return out
+
+
+def with_channel_outliers(arrays, seed: int, n_channels: int = 2, factor: float = 10.0) -> list[np.ndarray]:
+    """Copies of float32 samples [..., d] in which the same ``n_channels``
+    feature coordinates (chosen by PCG64 seeded with (seed, 4)) are
+    multiplied by ``factor`` in every array: outlier feature channels shared
+    by Q and K, the large coordinates that incoherent processing spreads."""
+    d = arrays[0].shape[-1]
+    rng = np.random.default_rng([seed, 4])
+    ch = rng.choice(d, n_channels, replace=False)
+    out = []
+    for a in arrays:
+        b = np.array(a, dtype=np.float32, copy=True)
+        b[..., ch] *= np.float32(factor)
+        out.append(b)
     return out

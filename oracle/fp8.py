@@ -29,7 +29,9 @@ What it computes, and where that is described:
     2^t with amax <= 448 * 2^t, so no value saturates.
   - The attention itself is then exact (float64) on the dequantised values.
     The kernel also rounds P to FP8 before the P V product; that rounding is
-    not modelled here, and the tests bound its effect (``p_error_bound``).
+    not modelled here, and the tests bound its effect (``p_rounding_bound``,
+    derived from the E4M3 format's spacing and pinned against a simulation of
+    that rounding).
 
 * The exact attention that the FP8 path approximates is the three-pass
   definition of ``oracle.attention``.
@@ -51,6 +53,7 @@ __all__ = [
     "quantize_v",
     "attention_forward_fp8",
     "attention_forward_fp8_rows",
+    "p_rounding_bound",
 ]
 
 E4M3_MAX = 448.0
@@ -155,21 +158,38 @@ def _dequant_v(codes, t, n):
     return np.swapaxes(_dequant_rows(codes, t), -1, -2)[..., :n, :]
 
 
+def p_rounding_bound(p, vd) -> np.ndarray:
+    """Bound on how far rounding the weights to E4M3 can move the output.
+
+    ``p`` [..., M, N] holds normalised weights (rows sum to 1, hidden keys
+    0), ``vd`` [..., N, d] the values.  A kernel evaluates the weights
+    unnormalised, p'_j = 2^(x_j - m) against a reference m at most 8 (log2
+    units) below the row maximum, so the largest p'_j of a row lies in
+    [1, 2^8], below the largest finite E4M3 value.  Rounding p'_j to nearest
+    E4M3 moves it by at most half a spacing: 2^-4 p'_j where p'_j >= 2^-6 (3
+    mantissa bits), and 2^-10 = 2^-4 2^-6 below that (the subnormal spacing
+    is 2^-9).  Divided by the row sum l >= max_j p'_j >= 1, the normalised
+    weight P_j moves by at most 2^-4 max(P_j, 2^-6 max_j P_j).  So each
+    output element O_ic moves by at most 2^-4 times
+
+        sum over visible j of max(P_j, 2^-6 max_j P_j) |v_jc|,
+
+    which this function returns (without the factor 2^-4)."""
+    p = np.asarray(p, dtype=np.float64)
+    w = np.maximum(p, 2.0 ** -6 * p.max(axis=-1, keepdims=True))
+    w = np.where(p > 0, w, 0.0)     # hidden keys carry no weight
+    return w @ np.abs(np.asarray(vd, dtype=np.float64))
+
+
 def attention_forward_fp8(q, k, v, signs, causal: bool, scale: float, return_parts: bool = False):
     """FP8 forward as stated in the module docstring.
 
     ``q, k, v`` [B, H, N, d] (the exact input values), ``signs`` a length-d
     vector of +-1 (None: no rotation).  Returns (O, LSE) in float64, and with
     ``return_parts`` also a dict with the codes and exponents of Q, K, V,
-    the dequantised operands and ``p_error_bound`` [B, H, N, d].
-
-    The bound: a kernel that rounds each unnormalised weight p_j (largest
-    weight of the row >= 1) to E4M3 changes it by at most 2^-4 max(p_j, 2^-6)
-    (half an ulp of 3 mantissa bits; below the smallest normal 2^-6 the
-    spacing is 2^-9).  In normalised weights P_j that is at most
-    2^-4 max(P_j, 2^-6 max_j P_j), so O_ic moves by at most
-    2^-4 * sum_j max(P_j, 2^-6 max_j P_j) |v'_jc|; ``p_error_bound`` is that
-    sum (without the 2^-4)."""
+    the dequantised operands and ``p_error_bound`` [B, H, N, d]: the
+    ``p_rounding_bound`` of the weights and the dequantised V, i.e. how far
+    rounding the weights to E4M3 can move O, divided by 2^-4."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -195,9 +215,7 @@ def attention_forward_fp8(q, k, v, signs, causal: bool, scale: float, return_par
             o[b, h] = p @ vd[b, h]
             lse[b, h] = l
             if return_parts:
-                w = np.maximum(p, 2.0 ** -6 * p.max(axis=-1, keepdims=True))
-                w = np.where(p > 0, w, 0.0)     # hidden keys carry no weight
-                bound[b, h] = w @ np.abs(vd[b, h])
+                bound[b, h] = p_rounding_bound(p, vd[b, h])
     if not return_parts:
         return o, lse
     return o, lse, {"q8": q8, "qt": qt, "k8": k8, "kt": kt, "v8": v8, "vt": vt,
@@ -226,5 +244,4 @@ def attention_forward_fp8_rows(q_bh, k_bh, v_bh, rows, signs, causal: bool, scal
     kd = _dequant_rows(*quantize_rows(kr))
     vd = _dequant_v(*quantize_v(v), n)
     p, lse = softmax_rows(scores(qd, kd, causal, s_scale, rows=rows))
-    w = np.where(p > 0, np.maximum(p, 2.0 ** -6 * p.max(axis=-1, keepdims=True)), 0.0)
-    return p @ vd, lse, w @ np.abs(vd)
+    return p @ vd, lse, p_rounding_bound(p, vd)

@@ -135,14 +135,11 @@ def test_fp8_halves_equal_whole(fa):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
-def test_rotation_lowers_outlier_error(fa):
-    """0.1% of the entries of Q and K multiplied by 10: FP8 error against
-    exact attention (of the bf16 inputs) with and without the rotation."""
+def _rotation_ratio(fa, q, k, v):
+    """RMSE of the FP8 forward against exact attention of the bf16 inputs,
+    without and with the rotation."""
     import torch
 
-    B, H, N = 1, 4, 1024
-    q, k, v = fi.draw_f32(21, (B, H, N, D), 3)
-    q, k = fi.with_outliers(q, 21), fi.with_outliers(k, 22)
     qb, kb, vb = (fi.f32_to_bf16_bits(a) for a in (q, k, v))
     tq, tk, tv = dev(qb), dev(kb), dev(vb)
     ref, _ = attention_forward(fi.exact_f64(qb), fi.exact_f64(kb), fi.exact_f64(vb), False, D ** -0.5)
@@ -151,8 +148,27 @@ def test_rotation_lowers_outlier_error(fa):
     torch.cuda.synchronize()
     e_plain = float(np.sqrt(np.mean((host64(o_plain) - ref) ** 2)))
     e_rot = float(np.sqrt(np.mean((host64(o_rot) - ref) ** 2)))
-    print(f"FP8 RMSE vs exact: plain {e_plain:.4g}, rotated {e_rot:.4g}, ratio {e_plain / e_rot:.3g}")
-    assert e_rot * 1.25 < e_plain
+    return e_plain, e_rot
+
+
+def test_rotation_lowers_outlier_error(fa):
+    """The FlashAttention-3 page: the rotation lowers the FP8 error about 2.6x
+    on inputs with outliers.  Two feature channels shared by Q and K carry
+    outliers (x10); the rotation must lower the RMSE against exact attention
+    at least 2x.  Isolated outlier entries (0.1% of the entries x10), which
+    the rotation helps less, must still see a lower error."""
+    B, H, N = 1, 4, 1024
+    q, k, v = fi.draw_f32(21, (B, H, N, D), 3)
+    qc, kc = fi.with_channel_outliers([q, k], 21)
+    e_plain, e_rot = _rotation_ratio(fa, qc, kc, v)
+    print(f"FP8 RMSE vs exact, channel outliers: plain {e_plain:.4g}, rotated {e_rot:.4g}, "
+          f"ratio {e_plain / e_rot:.3g}")
+    assert e_rot * 2.0 < e_plain
+    qs, ks = fi.with_outliers(q, 21), fi.with_outliers(k, 22)
+    e_plain, e_rot = _rotation_ratio(fa, qs, ks, v)
+    print(f"FP8 RMSE vs exact, isolated outliers: plain {e_plain:.4g}, rotated {e_rot:.4g}, "
+          f"ratio {e_plain / e_rot:.3g}")
+    assert e_rot < e_plain
 
 
 def test_full_size_fp8(fa):

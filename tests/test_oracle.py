@@ -192,6 +192,11 @@ FP8_MUTANTS = [
     ("_dequant_v", "np.swapaxes(_dequant_rows(codes, t), -1, -2)[..., :n, :]",
      "_dequant_rows(codes, t)[..., :n]"),                                              # V used untransposed
     ("e4m3_decode", "(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),                            # wrong mantissa width
+    ("p_rounding_bound", "return w @ np.abs(", "return 0.5 * w @ np.abs("),          # bound half as large
+    ("p_rounding_bound", "return w @ np.abs(", "return 2.0 * w @ np.abs("),          # bound twice as large
+    ("p_rounding_bound", "np.maximum(p, 2.0 ** -6 * p.max", "np.maximum(p, 0.0 * p.max"),  # no subnormal floor
+    ("p_rounding_bound", "np.maximum(p, 2.0 ** -6 * p.max", "np.maximum(p, 2.0 ** -5 * p.max"),  # floor too high
+    ("p_rounding_bound", "w @ np.abs(np.asarray(vd", "w @ (np.asarray(vd"),          # |v| dropped
 ]
 
 
