@@ -194,12 +194,30 @@ def _sample_rows(N, n, rng):
     return np.array(sorted(r for r in rows if 0 <= r < N))
 
 
+def _parallel(fn, tasks):
+    """Run fn over tasks on the host cores (numpy releases the GIL inside
+    its loops and products), with one BLAS thread per worker."""
+    import concurrent.futures as cf
+    import os
+
+    from threadpoolctl import threadpool_limits
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=1):
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, tasks))
+
+
+def _report(name, what, err, floor, n):
+    print(f"PARITY {name} {what}: max_abs_err {err:.5g} storage_floor {floor:.5g} elements {n}", flush=True)
+
+
 @pytest.mark.parametrize("name", FULL_FWD)
 def test_full_size_forward(fa, name):
-    """Full-size workloads in the benchmark's launch configuration, checked on
-    sampled (batch, head, row) outputs the oracle computes one by one, plus
-    output-wide properties: every element written and finite, bit-identical
-    on a repeated launch."""
+    """Full-size workloads in the benchmark's launch configuration, compared
+    with the oracle on EVERY element of O and LSE (the oracle runs per
+    (batch, head) in slabs of query rows); every element written (outputs
+    prefilled with NaN) and bit-identical on a repeated launch."""
     import torch
 
     w = fi.WORKLOADS[name]
@@ -214,26 +232,32 @@ def test_full_size_forward(fa, name):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
-
-    rng = np.random.default_rng(1)
-    heads = {(0, 0), (w.B - 1, w.H - 1)}
-    heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
     oh, lh = host64(o), host64(lse)
-    worst_o = worst_l = 0.0
-    for (b, h) in sorted(heads):
-        rows = _sample_rows(w.N, 96, rng)
+    del o2, lse2, tq, tk, tv
+
+    slab = min(w.N, 2048)
+    tasks = [(b, h, r0) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, slab)]
+
+    def one(t):
+        b, h, r0 = t
+        rows = np.arange(r0, min(w.N, r0 + slab))
         ro, rl = oracle.attention_forward_rows(fi.exact_f64(x["q"][b, h]), fi.exact_f64(x["k"][b, h]),
                                                fi.exact_f64(x["v"][b, h]), rows, w.causal, w.scale)
-        worst_o = max(worst_o, max_abs(oh[b, h, rows], ro))
-        worst_l = max(worst_l, max_abs(lh[b, h, rows], rl))
-    assert worst_o <= TOL_BF16, worst_o
-    assert worst_l <= TOL_LSE, worst_l
+        return (max_abs(oh[b, h, rows], ro), max_abs(lh[b, h, rows], rl), storage_floor(ro))
+
+    res = np.array(_parallel(one, tasks))
+    eo, el, fl = (float(res[:, i].max()) for i in range(3))
+    _report(name, "O", eo, fl, oh.size)
+    _report(name, "LSE", el, 0.0, lh.size)
+    assert eo <= TOL_BF16, f"O error {eo:.4g} (storage floor {fl:.3g})"
+    assert el <= TOL_LSE, f"LSE error {el:.4g}"
 
 
 def test_full_size_backward(fa):
-    """The forward+backward workload B=8, H=16, N=2048, d=128, causal: dQ, dK,
-    dV on sampled whole heads against the oracle; whole outputs written,
-    finite and bit-identical on a repeated launch."""
+    """The forward+backward workload B=8, H=16, N=2048, d=128, causal: dQ, dK
+    and dV compared with the oracle on EVERY element of all 128 heads; whole
+    outputs written (prefilled with NaN), finite and bit-identical on a
+    repeated launch."""
     import torch
 
     w = fi.WORKLOADS["bf16_b8h16n2048d128_causal_fwdbwd"]
@@ -252,17 +276,20 @@ def test_full_size_backward(fa):
     for a, b in zip(grads, again):
         assert bool(torch.isfinite(a).all())
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-
-    rng = np.random.default_rng(2)
-    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
     got = [host64(t) for t in grads]
-    for (b, h) in sorted(heads):
+    del again, grads
+
+    def one(t):
+        b, h = t
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = oracle.attention_backward(*(fi.exact_f64(x[n][sl]) for n in ("q", "k", "v", "do")), True, w.scale)
-        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-            e = max_abs(g[sl], r)
-            assert e <= TOL_BF16, f"{name} head {(b, h)}: {e:.4g} (storage floor {storage_floor(r):.3g})"
+        return [v for g, r in zip(got, ref) for v in (max_abs(g[sl], r), storage_floor(r))]
 
+    res = np.array(_parallel(one, [(b, h) for b in range(w.B) for h in range(w.H)]))
+    for i, name in enumerate(("dQ", "dK", "dV")):
+        e, f = float(res[:, 2 * i].max()), float(res[:, 2 * i + 1].max())
+        _report(w.name, name, e, f, got[i].size)
+        assert e <= TOL_BF16, f"{name}: {e:.4g} (storage floor {f:.3g})"
 
 
 # (B, H, N, d, causal): up to 512 workgroups per grid at d=128 (768 at d=64)
