@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import FA_ERR_UNSUPPORTED, FA_OK, FaLibraryMissing, load  # noqa: F401
+from ._lib import FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED, FA_OK, NOALLOC_SCRATCH_BYTES, FaLibraryMissing, load  # noqa: F401
 
 __all__ = [
     "FaError",
@@ -37,6 +37,8 @@ __all__ = [
     "fa_backward_dq",
     "fa_backward_dq_delta",
     "fa_backward_workspace_size",
+    "fa_backward_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "fa_status_string",
     "fa_abi_version",
     "forward",
@@ -139,6 +141,11 @@ def fa_backward_f32(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, 
 
 def fa_backward_workspace_size(B, H, N, d) -> int:
     return int(_call("fa_backward_workspace_size", B, H, N, d))
+
+
+def fa_backward_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, stream) -> int:
+    return _call("fa_backward_noalloc", q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                 stream)
 
 
 def fa_status_string(status: int) -> str:

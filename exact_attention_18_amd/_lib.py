@@ -15,6 +15,8 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
+FA_ERR_TOO_LARGE = -4
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -39,6 +41,7 @@ SIGNATURES = {
     "fa_backward_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_backward_dq_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "fa_backward_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "fa_backward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_forward_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _vp]),
     "fa_backward_f32": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                              _vp, _sz, _vp]),

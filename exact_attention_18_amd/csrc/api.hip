@@ -4,10 +4,18 @@
 #include <stdlib.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "launch.h"
 
 extern "C" size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+// Scratch of fa_backward_noalloc: a file-scope device array, one copy per GPU.
+// Host code never uses this name as an address (on the host it names a
+// stand-in object); the device address comes from hipGetSymbolAddress, once
+// per device, with that device current, and is kept in noalloc_ptr.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -124,6 +132,24 @@ int backward_impl(const T* q, const T* k, const T* v, const T* o, const float* l
                                          scale, delta, s), stream);
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on first use.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (noalloc_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return FA_OK;
+}
+
 // Shared checks of the bf16 backward stages.  `ws_written` says whether the
 // stage writes the workspace (an output) or only reads it (an input).
 int stage_checks(int B, int H, int N, int d, int causal, float scale, const void* const* in_ptrs,
@@ -222,8 +248,35 @@ const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (pointer, size, scale, causal flag, alignment, overlap or workspace)";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension not supported by this entry point";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: the problem needs more than the static scratch buffer holds";
     default: return "unknown status";
   }
+}
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                        float scale, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_backward_workspace_size(B, H, N, d);
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  // the caller's buffers are checked before the first HIP call
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(lse, lb), span(dO, tb)};
+  const void* inp[6] = {q, k, v, o, lse, dO};
+  const Span outs[3] = {span(dq, tb), span(dk, tb), span(dv, tb)};
+  const void* outp[3] = {dq, dk, dv};
+  st = check_buffers(ins, inp, 6, outs, outp, 3);
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != FA_OK) return st;
+  return backward_impl(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse,
+                       static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+                       static_cast<uint16_t*>(dv), B, H, N, d, causal, scale, ws, FA_NOALLOC_SCRATCH_BYTES, stream,
+                       true);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {

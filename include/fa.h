@@ -31,7 +31,8 @@
  * LSE        lse[b][h][i] = log(sum_j exp(scale * q_i . k_j)) over the visible
  *            keys j, natural log, float32.
  * Ownership  The caller allocates and owns every buffer (device memory).  The
- *            library allocates nothing and keeps no state between calls.
+ *            library allocates nothing and keeps no state between calls, except
+ *            for fa_backward_noalloc's static scratch buffer (see there).
  * Aliasing   q, k and v may alias one another.  Every output buffer (o, lse,
  *            dq, dk, dv, workspace) must not overlap any other buffer passed to
  *            the same call.
@@ -60,14 +61,16 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, scale, causal flag,
                               misaligned or overlapping buffers, workspace too small */
   FA_ERR_UNSUPPORTED = -2, /* head dimension not supported by this entry point */
-  FA_ERR_HIP = -3          /* the HIP runtime reported a launch error */
+  FA_ERR_HIP = -3,         /* the HIP runtime reported a launch error */
+  FA_ERR_TOO_LARGE = -4    /* the problem needs more scratch than the library's
+                              static buffer holds (fa_backward_noalloc) */
 };
 
 /*
@@ -258,6 +261,32 @@ int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void
 /* Bytes of workspace fa_backward and fa_backward_f32 need for these sizes
  * (0 if a size is not positive).  Pure host function. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/* Bytes of the static device scratch buffer behind fa_backward_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * fa_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It computes exactly what
+ * fa_backward computes (same kernels, bit-identical outputs) and calls no
+ * allocating routine.  Its scratch (the rows -delta_i, 4*B*H*N bytes) is a
+ * file-scope device array of FA_NOALLOC_SCRATCH_BYTES bytes that each GPU
+ * the library runs on holds until the process ends; its address is looked
+ * up once per device, on the first call with that device current.
+ *   Arguments: as fa_backward, without workspace and workspace_bytes; the
+ *   stream must belong to the current device.
+ *   Returns FA_ERR_TOO_LARGE when 4*B*H*N (rounded up to 256) exceeds
+ *   FA_NOALLOC_SCRATCH_BYTES (B*H*N up to 4194304 rows fits), after the
+ *   same argument checks as fa_backward.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap in
+ * time on one GPU (different streams, or different host threads) race and
+ * must be serialised by the caller.  Calls on one stream are ordered and
+ * safe.
+ */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /* float32 debug twins of fa_forward / fa_backward: same arguments, same
  * layouts and semantics, float32 storage and arithmetic throughout. */

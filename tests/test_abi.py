@@ -39,7 +39,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3):
+    for code in (0, -1, -2, -3, -4):
         s = lib.fa_status_string(code).decode()
         assert s.startswith("FA_")
     assert lib.fa_status_string(7).decode() == "unknown status"
@@ -283,6 +283,50 @@ def test_block_sparse_workspace(lib):
     assert sparse(lib, ws=ptr(7), ws_bytes=need - 1) == INVALID         # too small
     assert sparse(lib, ws=ptr(7, 8), ws_bytes=need) == INVALID          # misaligned
     assert sparse(lib, ws=ptr(3, 16), ws_bytes=need) == INVALID         # inside o
+
+
+# ---- fa_backward_noalloc (static scratch): host-side rejections
+
+def bwd_noalloc(lib, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None):
+    p = ptrs or [ptr(i) for i in range(9)]
+    return lib.fa_backward_noalloc(*p, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=-1), dict(causal=3), dict(scale=-0.5), dict(scale=math.inf)])
+def test_noalloc_rejects_bad_sizes(lib, kw):
+    assert bwd_noalloc(lib, **kw) == INVALID
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_noalloc_rejects_unsupported_head_dim(lib, d):
+    assert bwd_noalloc(lib, d=d) == UNSUP
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_noalloc_rejects_null_misaligned_and_overlap(lib, which):
+    p = [ptr(i) for i in range(9)]
+    p[which] = None
+    assert bwd_noalloc(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(9)]
+    p[which] = ptr(which, 8)
+    assert bwd_noalloc(lib, ptrs=p) == INVALID
+    if which >= 6:   # an output starting inside another buffer
+        p = [ptr(i) for i in range(9)]
+        p[which] = ptr((which + 1) % 9, 16)
+        assert bwd_noalloc(lib, ptrs=p) == INVALID
+
+
+def test_noalloc_size_limit(lib):
+    rows = _lib.NOALLOC_SCRATCH_BYTES // 4
+    m = re.search(r"#define\s+FA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.fa_backward_workspace_size(1, 1, rows, 64) == _lib.NOALLOC_SCRATCH_BYTES
+    # the largest problem that fits passes the size check (and then fails on
+    # the fake pointers' overlap: every buffer is given the same address)
+    same = [ptr(0)] * 9
+    assert bwd_noalloc(lib, N=rows, ptrs=same) == INVALID
+    assert bwd_noalloc(lib, N=rows + 1) == _lib.FA_ERR_TOO_LARGE
+    assert bwd_noalloc(lib, B=2, H=3, N=rows // 6 + 1) == _lib.FA_ERR_TOO_LARGE
 
 
 # The stages of fa_backward: name -> (number of leading pointer arguments,
