@@ -102,12 +102,12 @@ struct TileDma {
 // s[kb] is key 32*kb + 8*(r/4) + 4*g + r%4): optional mask (keys past `lim`
 // get -inf), row max, and the lazy rescale of the reference max m, the row
 // sum and the output accumulators.
-template <int D, bool MASK>
-__device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D / 32], float& m, float& lsum, float c,
-                                               int lim) {
+template <int D, bool MASK, int NKB = 2>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[NKB], f32x16 (&oacc)[D / 32], float& m, float& lsum,
+                                               float c, int lim) {
   if (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
@@ -115,9 +115,9 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D 
   // Row max as a shallow tree (v_max3), not a 32-long dependent chain.
   // max_nan (NaN-propagating maximum) lowers to v_maximum3_f32 without the
   // operand canonicalisation that fmaxf needs in IEEE mode.
-  float m8[4];
+  float m8[2 * NKB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 8 * h;
@@ -126,6 +126,8 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D 
       m8[2 * kb + h] = max_nan(max_nan(a, b), max_nan(s[kb][r + 6], s[kb][r + 7]));
     }
   float mx = max_nan(max_nan(m8[0], m8[1]), max_nan(m8[2], m8[3]));
+#pragma unroll
+  for (int i = 4; i < 2 * NKB; i += 2) mx = max_nan(mx, max_nan(m8[i], m8[i + 1]));
   mx = max_halves(mx) * c;  // c > 0: the scaled row max over the tile (or -inf)
 
   // Raise the reference max only when some row's tile max exceeds it by
@@ -148,12 +150,12 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], f32x16 (&oacc)[D 
 // keeps m.  Otherwise (also while m is still -inf, which gives inf or NaN)
 // the tile takes softmax_update and P is recomputed with the new m, as if
 // the fast path had not run.  Sums are added in the same order either way.
-template <int D, bool MASK>
-__device__ __forceinline__ void softmax_probs(f32x16 (&s)[2], u32x4 (&pw)[4], f32x16 (&oacc)[D / 32], float& m,
-                                              float& lsum, float c, int lim) {
+template <int D, bool MASK, int NKB = 2>
+__device__ __forceinline__ void softmax_probs(f32x16 (&s)[NKB], u32x4 (&pw)[2 * NKB], f32x16 (&oacc)[D / 32],
+                                              float& m, float& lsum, float c, int lim) {
   if (MASK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
@@ -161,7 +163,7 @@ __device__ __forceinline__ void softmax_probs(f32x16 (&s)[2], u32x4 (&pw)[4], f3
   auto probs = [&](float& l) {
     float bmax = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float ps[4];
@@ -182,7 +184,7 @@ __device__ __forceinline__ void softmax_probs(f32x16 (&s)[2], u32x4 (&pw)[4], f3
   float l = lsum;
   const float bmax = probs(l);
   if (__any(!(bmax <= PMAX))) {
-    softmax_update<D, false>(s, oacc, m, lsum, c, 0);
+    softmax_update<D, false, NKB>(s, oacc, m, lsum, c, 0);
     l = lsum;
     probs(l);
   }
@@ -243,6 +245,23 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
         oacc[db] = mfma32(a, pb, oacc[db]);
       }
     }
+}
+
+// tile_step on the stage at (Ks, Vs), with the direct loads of the next
+// tile into the other stage (next) issued first.  The three stages are
+// disjoint; passing them as restrict pointers of one inlined function gives
+// the LDS accesses alias scopes, so the compiler can tell that the transpose
+// reads of this tile do not read what the loads write and does not make
+// them wait for the loads.
+template <int D, bool MASK, int NW>
+__device__ __forceinline__ void tile_step_next(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
+                                               uint16_t* __restrict__ next, bool load_next,
+                                               const TileDma<D, NW>& dma, __amdgpu_buffer_rsrc_t krs,
+                                               __amdgpu_buffer_rsrc_t vrs, int kv_next, int wave,
+                                               const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& m,
+                                               float& lsum, float c, int lim, int lane) {
+  if (load_next) dma.issue(krs, vrs, kv_next, next, wave);
+  tile_step<D, MASK>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
 }
 
 #ifndef FA_FWD_WAVES_PER_SIMD
@@ -332,10 +351,12 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const uint16_t* Ks = smem + slot * L::STAGE;
       const uint16_t* Vs = Ks + L::K_ELEMS;
       const int kv0 = j * BC;
-      if (jn < ntiles) dma.issue(krs, vrs, jn * BC, smem + (slot ^ 1) * L::STAGE, wave);
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
-        tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
+        tile_step_next<D, true, NT / 64>(Ks, Vs, smem + (slot ^ 1) * L::STAGE, jn < ntiles, dma, krs, vrs, jn * BC,
+                                        wave, qf, oacc, m, lsum, c, lim, lane);
+      } else if (jn < ntiles) {
+        dma.issue(krs, vrs, jn * BC, smem + (slot ^ 1) * L::STAGE, wave);
       }
       wait_vmem();
       __syncthreads();
@@ -356,15 +377,19 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* Ks = smem + (j & 1) * L::STAGE;
     const uint16_t* Vs = Ks + L::K_ELEMS;
+    uint16_t* next = smem + ((j + 1) & 1) * L::STAGE;
     const int kv0 = j * BC;
-    if (j + 1 < ntiles) dma.issue(krs, vrs, kv0 + BC, smem + ((j + 1) & 1) * L::STAGE, wave);
     if constexpr (MASK) {
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
-        tile_step<D, true>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
+        tile_step_next<D, true, NT / 64>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf, oacc, m,
+                                        lsum, c, lim, lane);
+      } else if (j + 1 < ntiles) {
+        dma.issue(krs, vrs, kv0 + BC, next, wave);
       }
     } else {
-      tile_step<D, false>(Ks, Vs, qf, oacc, m, lsum, c, 0, lane);
+      tile_step_next<D, false, NT / 64>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf, oacc, m,
+                                       lsum, c, 0, lane);
     }
     wait_vmem();
     __syncthreads();
@@ -403,116 +428,22 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // waves owns 256 queries; waves w and w+4 run on the same SIMD (the
 // dispatcher places the waves of a workgroup on the 4 SIMDs in turn), group 0
 // is waves 0-3 and group 1 waves 4-7.  Each wave alternates
-//   matrix phase k:  S(k) = K(k) Q^T (64 keys) and O^T += V(k-1)^T P(k-1)^T
+//   matrix phase k:  O^T += V(k-1)^T P(k-1)^T and S(k) = K(k) Q^T (128 keys)
 //   softmax phase k: mask, row max and lazy rescale on S(k), P(k) = exp2(...)
 // and the groups run them one phase apart, with a workgroup barrier between
 // phases: in every phase one wave per SIMD keeps the matrix core busy while
-// the other wave's softmax runs on the vector ALU.  Per query the arithmetic
-// and its order are those of fwd_bf16_kernel (same tiles in the same order,
-// same lazy rescale, same sums), so the results are identical.
+// the other wave's softmax runs on the vector ALU.
 //
 // Phase pair k: group 0 runs matrix phase k then softmax phase k; group 1
 // runs softmax phase k-1 then matrix phase k.  Tiles K(k+1) and V(k) are
-// written to LDS during pair k, each group storing half of them in its
-// softmax phase, from registers it fetched from HBM one pair earlier; their
+// loaded straight into LDS during pair k (every wave issues its share at the
+// start of the pair and waits for it before the pair's last barrier); their
 // slots held K(k-1) and V(k-2), whose last reads were in pair k-1.  The
 // barriers are also scheduling fences, so no instruction migrates from one
 // phase into the next.
 constexpr int PP_BR = 256;              // queries per workgroup
 constexpr int PP_NT = 512;              // 8 waves
 constexpr int PP_MIN_CAUSAL_N = 2049;   // shorter causal problems use fwd_bf16_kernel
-
-template <int D>
-struct PpLds {
-  static constexpr int KS = D + FA_FWD_KPAD;
-  static constexpr int VS = D + FA_FWD_VPAD;
-  static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = BC * VS;
-  static constexpr int V0 = 2 * K_ELEMS;                   // K slots 0, 1, then V slots 0, 1
-  static constexpr int ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;
-  static constexpr int CPR = D / 8;                        // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / PP_NT;             // chunks per thread for a whole tile
-  static constexpr int HALF = BC * CPR / 2;                // chunks in half a tile
-};
-
-// HBM -> registers and registers -> LDS for chunks [first, first + CPT * step)
-// of a 64-row tile, `step` apart (a whole tile: first = tid, step = 512; a
-// group's half: first = half * HALF + thread-in-group, step = 256).  Rows at
-// or past N read as zero (buffer bounds).
-template <int D>
-__device__ __forceinline__ void pp_load(u32x4 (&r)[PpLds<D>::CPT], __amdgpu_buffer_rsrc_t rs, int kv0, int first,
-                                        int step) {
-  using L = PpLds<D>;
-#pragma unroll
-  for (int i = 0; i < L::CPT; ++i) {
-    const int c = first + step * i;
-    r[i] = buf_load16(rs, (uint32_t)(((kv0 + c / L::CPR) * D + (c % L::CPR) * 8) * 2));
-  }
-}
-template <int D, int STRIDE>
-__device__ __forceinline__ void pp_store(const u32x4 (&r)[PpLds<D>::CPT], uint16_t* dst, int first, int step) {
-  using L = PpLds<D>;
-#pragma unroll
-  for (int i = 0; i < L::CPT; ++i) {
-    const int c = first + step * i;
-    *reinterpret_cast<u32x4*>(dst + (c / L::CPR) * STRIDE + (c % L::CPR) * 8) = r[i];
-  }
-}
-
-// Matrix phase: S = K Q^T on the tile at Ks (QK), then O^T += V^T P^T on
-// the tile at Vs with P packed in pw (PV).
-template <int D, bool QK, bool PV>
-__device__ __forceinline__ void pp_matrix(const uint16_t* Ks, const uint16_t* Vs, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&s)[2], const u32x4 (&pw)[4], f32x16 (&oacc)[D / 32],
-                                          int lane) {
-  using L = PpLds<D>;
-  constexpr int KSTEPS = D / 16, DB = D / 32;
-  const int l32 = lane & 31, g = lane >> 5;
-  if (QK) {
-    const uint16_t* krow = Ks + l32 * L::KS + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = mfma32(bf16x8_from(*reinterpret_cast<const u32x4*>(krow + kb * 32 * L::KS + ks * 16)), qf[ks],
-                       ks == 0 ? f32x16{} : s[kb]);
-  }
-  if (PV) {
-    const int tr_row = 4 * g + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint16_t* vp = Vs + ((b >> 1) * 32 + 16 * (b & 1) + tr_row) * L::VS + tr_col;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        oacc[db] = mfma32(bf16x8_from(lds_read_tr16(vp + db * 32), lds_read_tr16(vp + 8 * L::VS + db * 32)),
-                          __builtin_bit_cast(bf16x8, pw[b]), oacc[db]);
-    }
-  }
-  // Eight LDS reads (mask 0x100) ahead of the products (mask 0x008), then
-  // one or two reads per product.
-  constexpr int NM = (QK ? 2 * KSTEPS : 0) + (PV ? 4 * DB : 0);
-  constexpr int NR = (QK ? 2 * KSTEPS : 0) + (PV ? 8 * DB : 0);
-  constexpr int AHEAD = NR < 8 ? NR : 8;
-  constexpr int R2 = NR - AHEAD - NM > 0 ? NR - AHEAD - NM : 0;
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < R2)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    else
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// Softmax phase: softmax_probs on S (P packed to bf16 into pw, row sum into
-// lsum), exactly as tile_step does it.
-template <int D, bool MASK>
-__device__ __forceinline__ void pp_softmax(f32x16 (&s)[2], u32x4 (&pw)[4], f32x16 (&oacc)[D / 32], float& m,
-                                           float& lsum, float c, int lim) {
-  softmax_probs<D, MASK>(s, pw, oacc, m, lsum, c, lim);
-}
 
 // Workgroup barrier that is also a scheduling fence.
 __device__ __forceinline__ void pp_sync() {
@@ -521,169 +452,361 @@ __device__ __forceinline__ void pp_sync() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool CAUSAL>
+// Online softmax over a 128-key tile (four 32-key blocks of S^T, element r
+// of s[kb] is key 32 kb + 8 (r/4) + 4 g + r%4), with P written back into the
+// registers of S: word e of P block b = 2 kb + t (keys 32 kb + 16 t + ...)
+// goes to s[kb][8 t + e].  The row max comes first (so S need not stay live
+// beside P); the reference max m is raised only when the tile's max exceeds
+// it by more than TAU, as in softmax_update, and the arithmetic per element
+// is that of softmax_probs.
+template <bool MASK>
+__device__ __forceinline__ void softmax_inplace128(f32x16 (&s)[4], f32x16 (&oacc)[4], float& m, float& lsum, float c,
+                                                   int lim) {
+  softmax_update<128, MASK, 4>(s, oacc, m, lsum, c, lim);
+  float l = lsum;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float ps[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 8 * t + 2 * e;
+        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, -m));
+        ps[e] = p0 + p1;
+        s[kb][8 * t + e] = __uint_as_float(pack_bf16x2(p0, p1));   // elements 8t+e <= r were read already
+      }
+      l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+  lsum = l;
+}
+
+// Tiles of 128 keys: a matrix phase is 64 products per wave, so the
+// per-phase costs (the barrier, the first LDS reads of a phase, the first
+// read of the new scores) are paid half as often per product as with 64-key
+// tiles.  P(k-1) V(k-1) goes first so that P's registers (which are S's,
+// see softmax_inplace128) are free before S(k) is written.
+//
+// Work items are (batch*head, 256-query block) pairs, heaviest first when
+// the mask makes the work grow with the block index; when B*H is a multiple
+// of 8 the workgroups of each XCD (id % 8) take only the heads h with h % 8
+// equal to their XCD, so a head's K and V are read through one L2.  With
+// PERSIST (not built by default: the loop's extra live values do not fit the
+// register budget), one workgroup per compute unit walks a list of items
+// dealt in a serpentine (round t to workgroups 0, 1, ... when t is even and
+// in the reverse order when t is odd).
+constexpr int PP_BK = 128;   // keys per tile
+
+struct PpLds {
+  static constexpr int D = 128;
+  static constexpr int KS = D + FA_FWD_KPAD;
+  static constexpr int VS = D + FA_FWD_VPAD;
+  static constexpr int K_ELEMS = PP_BK * KS;
+  static constexpr int V_ELEMS = PP_BK * VS;
+  static constexpr int V0 = 2 * K_ELEMS;                   // K slots 0, 1, then V slots 0, 1
+  static constexpr int ELEMS = 2 * K_ELEMS + 2 * V_ELEMS;
+  // direct loads of 64 x 16 bytes fill a tile's padded rows in order
+  static constexpr int KCPR = KS / 8, VCPR = VS / 8;       // chunks per padded row
+  static constexpr int KLOADS = PP_BK * KCPR / 64, VLOADS = PP_BK * VCPR / 64;
+  static_assert(KLOADS * 64 == PP_BK * KCPR && VLOADS * 64 == PP_BK * VCPR, "tiles must be whole loads");
+  static_assert(ELEMS * 2 <= 160 * 1024, "two K and two V tiles fit in the LDS");
+};
+
+// Direct HBM -> LDS loads of 128-row tiles shared out over the 8 waves: load
+// j of a K tile (or of a V tile) is issued by wave j % 8; lane l of a load
+// fills 16-byte chunk 64 (its index within the tile) + l of the tile's
+// padded rows.  A lane on a row's padding loads the row's first chunk again
+// (the padding is never read).  The buffer resource starts at the tile's
+// first row and ends at row N, so rows at or past N read as zero and the
+// per-lane offsets stay the same for every tile.
+struct PpDma {
+  using L = PpLds;
+  static constexpr int PK = (L::KLOADS + 7) / 8, PV = (L::VLOADS + 7) / 8;
+  uint32_t koff[PK], voff[PV];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int p = 64 * (wave + 8 * u) + lane, row = p / L::KCPR, col = p % L::KCPR;
+      koff[u] = (uint32_t)(row * L::D + (col < L::D / 8 ? col * 8 : 0)) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const int p = 64 * (wave + 8 * u) + lane, row = p / L::VCPR, col = p % L::VCPR;
+      voff[u] = (uint32_t)(row * L::D + (col < L::D / 8 ? col * 8 : 0)) * 2;
+    }
+  }
+  // rows kv0 .. of the head at src (N rows) into the tile at dst
+  __device__ __forceinline__ void k_tile(const uint16_t* src, int N, int kv0, uint16_t* dst, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (size_t)kv0 * L::D, (uint32_t)(N - kv0) * L::D * 2);
+#pragma unroll
+    for (int u = 0; u < PK; ++u)
+      if (wave + 8 * u < L::KLOADS) lds_load16(rs, dst + (wave + 8 * u) * 512, koff[u]);
+  }
+  __device__ __forceinline__ void v_tile(const uint16_t* src, int N, int kv0, uint16_t* dst, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (size_t)kv0 * L::D, (uint32_t)(N - kv0) * L::D * 2);
+#pragma unroll
+    for (int u = 0; u < PV; ++u)
+      if (wave + 8 * u < L::VLOADS) lds_load16(rs, dst + (wave + 8 * u) * 512, voff[u]);
+  }
+};
+
+// Matrix phase over one 128-key tile: O^T += V^T P^T on the tile at Vs (PV),
+// then S = K Q^T on the tile at Ks (QK).
+template <bool QK, bool PV>
+__device__ __forceinline__ void pp_matrix(const uint16_t* Ks, const uint16_t* Vs, const bf16x8 (&qf)[8],
+                                          f32x16 (&s)[4], f32x16 (&oacc)[4], int lane) {
+  using L = PpLds;
+  const int l32 = lane & 31, g = lane >> 5;
+  if (PV) {
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint16_t* vp = Vs + ((b >> 1) * 32 + 16 * (b & 1) + tr_row) * L::VS + tr_col;
+      {
+        const int kb = b >> 1, t8 = 8 * (b & 1);
+        const u32x4 pb = {__float_as_uint(s[kb][t8]), __float_as_uint(s[kb][t8 + 1]), __float_as_uint(s[kb][t8 + 2]),
+                          __float_as_uint(s[kb][t8 + 3])};
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          oacc[db] = mfma32(bf16x8_from(lds_read_tr16(vp + db * 32), lds_read_tr16(vp + 8 * L::VS + db * 32)),
+                            __builtin_bit_cast(bf16x8, pb), oacc[db]);
+      }
+    }
+    // two reads per product, eight ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // P is dead once these products are issued; S is written only after
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (QK) {
+    const uint16_t* krow = Ks + l32 * L::KS + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        s[kb] = mfma32(bf16x8_from(*reinterpret_cast<const u32x4*>(krow + kb * 32 * L::KS + ks * 16)), qf[ks],
+                       ks == 0 ? f32x16{} : s[kb]);
+  }
+  if (QK) {
+    // one read per product, eight ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+}
+
+// The loads of a pair and the LDS reads that follow them, with every LDS
+// stage passed as a restrict pointer of one inlined function (K(k), V(k-1)
+// read; K(k+1), V(k) written: four disjoint slots), so that the compiler can
+// tell that the transpose reads do not read what the loads write and does
+// not make them wait for the loads.  Group 0: loads, then its matrix phase.
+// Group 1: loads, its softmax phase (sm), the barrier between the phases,
+// then its matrix phase.
+template <bool QK, bool PV>
+__device__ __forceinline__ void pp_load_matrix(const uint16_t* __restrict__ Kr, const uint16_t* __restrict__ Vr,
+                                               uint16_t* __restrict__ Kw, uint16_t* __restrict__ Vw, bool load_k,
+                                               bool load_v, bool mat, const PpDma& dma, const uint16_t* K,
+                                               const uint16_t* V, int N, int kv_k, int kv_v, int wave,
+                                               const bf16x8 (&qf)[8], f32x16 (&s)[4], f32x16 (&oacc)[4], int lane) {
+  if (load_k) dma.k_tile(K, N, kv_k, Kw, wave);
+  if (load_v) dma.v_tile(V, N, kv_v, Vw, wave);
+  if (mat) pp_matrix<QK, PV>(Kr, Vr, qf, s, oacc, lane);
+}
+template <bool QK, bool PV, class SM>
+__device__ __forceinline__ void pp_load_softmax_matrix(const uint16_t* __restrict__ Kr,
+                                                       const uint16_t* __restrict__ Vr, uint16_t* __restrict__ Kw,
+                                                       uint16_t* __restrict__ Vw, bool load_k, bool load_v, bool mat,
+                                                       const PpDma& dma, const uint16_t* K, const uint16_t* V, int N,
+                                                       int kv_k, int kv_v, int wave, const bf16x8 (&qf)[8],
+                                                       f32x16 (&s)[4], f32x16 (&oacc)[4], int lane, SM&& sm) {
+  if (load_k) dma.k_tile(K, N, kv_k, Kw, wave);
+  if (load_v) dma.v_tile(V, N, kv_v, Vw, wave);
+  sm();
+  pp_sync();
+  if (mat) pp_matrix<QK, PV>(Kr, Vr, qf, s, oacc, lane);
+}
+
+template <bool CAUSAL, bool PERSIST>
 __global__ void __launch_bounds__(PP_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-              uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int total, float c) {
+               uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int BH, float c) {
   constexpr int D = 128;
-  using L = PpLds<D>;
+  using L = PpLds;
   constexpr int KSTEPS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
   const int grp = wave >> 2;
-  const int gt = tid & (PP_NT / 2 - 1);   // thread within the group
-  const int l32 = lane & 31, g = lane >> 5;
-  int bh, qb;
-  map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
-  const size_t base = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
-  const int q0 = qb * PP_BR;
-  // The two waves of a SIMD take adjacent 32-query slices, so both groups
-  // meet the causal diagonal in the same tiles.
-  const int qw = q0 + 64 * (wave & 3) + 32 * grp;
-  const int myq = qw + l32;
+  const int g = lane >> 5, l32 = lane & 31;
 
-  bf16x8 qf[KSTEPS];
+  // item list of this workgroup (see above)
+  const int G = gridDim.x;
+  const int nx = (BH % 8 == 0 && G % 8 == 0) ? 8 : 1;
+  const int xg = blockIdx.x % nx, wl = blockIdx.x / nx, GL = G / nx;
+  const int hx = BH / nx, count = hx * nqb;
+  PpDma dma;
+  dma.init(wave, lane);
+
+  for (int t = 0; PERSIST || t < 1; ++t) {
+    const int r = t * GL + ((t & 1) ? GL - 1 - wl : wl);
+    if (r >= count) break;
+    const int hl = CAUSAL ? r % hx : r / nqb;
+    const int qb = CAUSAL ? nqb - 1 - r / hx : r % nqb;
+    const int bh = hl * nx + xg;
+
+    const size_t base = (size_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+    const int q0 = qb * PP_BR;
+    // The two waves of a SIMD take adjacent 32-query slices, so both groups
+    // meet the causal diagonal in the same tiles.
+    const int qw = q0 + 64 * (wave & 3) + 32 * grp;
+    const int myq = qw + l32;
+
+    bf16x8 qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
-    qf[ks] = bf16x8_from(buf_load16(qrs, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2)));
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[ks] = bf16x8_from(buf_load16(qrs, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2)));
 
-  const int kv_end = CAUSAL ? min(N, q0 + PP_BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
-  // Last tile this wave sees, and the first one that needs the mask (it has
-  // a key past one of the wave's queries, or past N).
-  const int last_w = CAUSAL ? min(qw + 31, N - 1) / BC : ntiles - 1;
-  const int first_mask_w = min(CAUSAL ? (qw + 1) / BC : ntiles, N / BC);
+    const int kv_end = CAUSAL ? min(N, q0 + PP_BR) : N;
+    const int ntiles = (kv_end + PP_BK - 1) / PP_BK;
+    // Last tile this wave sees, and the first one that needs the mask (it
+    // has a key past one of the wave's queries, or past N).
+    const int last_w = CAUSAL ? min(qw + 31, N - 1) / PP_BK : ntiles - 1;
+    const int first_mask_w = min(CAUSAL ? (qw + 1) / PP_BK : ntiles, N / PP_BK);
 
-  f32x16 oacc[DB];
+    f32x16 oacc[DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
-  f32x16 s[2];
-  u32x4 pw[4];
-  u32x4 rk[L::CPT], rv[L::CPT];
-  auto kslot = [&](int j) { return smem + (j & 1) * L::K_ELEMS; };
-  auto vslot = [&](int j) { return smem + L::V0 + (j & 1) * L::V_ELEMS; };
-  auto fetch = [&](int k) {   // this group's half of K(k+1) and V(k), HBM -> registers
-    if (k + 1 < ntiles) pp_load<D>(rk, krs, (k + 1) * BC, grp * L::HALF + gt, PP_NT / 2);
-    if (k < ntiles) pp_load<D>(rv, vrs, k * BC, grp * L::HALF + gt, PP_NT / 2);
-  };
-  auto store = [&](int k) {   // ... registers -> LDS
-    if (k + 1 < ntiles) pp_store<D, L::KS>(rk, kslot(k + 1), grp * L::HALF + gt, PP_NT / 2);
-    if (k < ntiles) pp_store<D, L::VS>(rv, vslot(k), grp * L::HALF + gt, PP_NT / 2);
-  };
-  // Softmax phase i; a tile the wave does not see (causal) gives P = 0.
-  auto softmax = [&](int i, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    if (i > last_w) {
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+    f32x16 s[4];   // S of the tile in flight, then its P (softmax_inplace128)
+    auto kslot = [&](int j) { return smem + (j & 1) * L::K_ELEMS; };
+    auto vslot = [&](int j) { return smem + L::V0 + (j & 1) * L::V_ELEMS; };
+    // Loads of pair k (both groups, at its start): K(k+1) and V(k) into the
+    // slots of K(k-1) and V(k-2), whose last reads were in pair k-1; each
+    // wave waits for its own loads before the barrier that ends pair k.
+    // Softmax phase i; a tile the wave does not see (causal) gives P = 0.
+    auto softmax = [&](int i, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      if (i > last_w) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) pw[b] = u32x4{0u, 0u, 0u, 0u};
-      return;
-    }
-    const int lim = MASK ? (CAUSAL ? min(myq, N - 1) : N - 1) - i * BC - 4 * g : 0;
-    pp_softmax<D, MASK>(s, pw, oacc, m, lsum, c, lim);
-  };
-  auto matrix = [&](int k, auto qk_tag, auto pv_tag) {
-    pp_matrix<D, decltype(qk_tag)::value, decltype(pv_tag)::value>(kslot(k), vslot(k - 1), qf, s, pw, oacc, lane);
-  };
-  using T = std::true_type;
-  using F = std::false_type;
-  // Matrix phase k of the tiles that need the mask: when neither tile k
-  // nor tile k-1 holds a key this wave sees (both past its last query), the
-  // phase is skipped (the scores would go unused and P is zero); the
-  // barriers stay the same for every wave.
-  auto matrix_tail = [&](int k) {
-    if (k - 1 <= last_w) matrix(k, T{}, T{});
-  };
-
-  {
-    // K(0), whole tile, in its own registers, so that this group's halves of
-    // K(1) and V(0) are in flight at the same time
-    u32x4 rk0[L::CPT];
-    pp_load<D>(rk0, krs, 0, tid, PP_NT);
-    fetch(0);
-    pp_store<D, L::KS>(rk0, kslot(0), tid, PP_NT);
-  }
-  pp_sync();
-
-  // Pairs 1 .. ntiles-1 run the full matrix phase; the pairs whose softmax
-  // needs no mask come first.  Both groups pass the same number of barriers.
-  const int k_mask = max(1, min(grp == 0 ? first_mask_w : first_mask_w + 1, ntiles));
-  if (grp == 0) {
-    matrix(0, T{}, F{});
-    pp_sync();
-    if (0 < first_mask_w) softmax(0, F{}); else softmax(0, T{});
-    store(0);
-    fetch(1);
-    pp_sync();
-    int k = 1;
-    for (; k < k_mask; ++k) {
-      matrix(k, T{}, T{});
-      pp_sync();
-      softmax(k, F{});
-      store(k);
-      fetch(k + 1);
-      pp_sync();
-    }
-    for (; k < ntiles; ++k) {
-      matrix_tail(k);
-      pp_sync();
-      softmax(k, T{});
-      store(k);
-      fetch(k + 1);
-      pp_sync();
-    }
-    if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
-    pp_sync();
-    pp_sync();
-  } else {
-    store(0);
-    fetch(1);
-    pp_sync();
-    matrix(0, T{}, F{});
-    pp_sync();
-    int k = 1;
-    for (; k < k_mask; ++k) {
-      softmax(k - 1, F{});
-      store(k);
-      fetch(k + 1);
-      pp_sync();
-      matrix(k, T{}, T{});
-      pp_sync();
-    }
-    for (; k < ntiles; ++k) {
-      softmax(k - 1, T{});
-      store(k);
-      fetch(k + 1);
-      pp_sync();
-      matrix_tail(k);
-      pp_sync();
-    }
-    if (ntiles - 1 < first_mask_w) softmax(ntiles - 1, F{}); else softmax(ntiles - 1, T{});
-    pp_sync();
-    if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
-    pp_sync();
-  }
-
-  const float ltot = sum_halves(lsum);
-  const float inv = ltot > 0.f ? rcp_hw(ltot) : 0.f;
-  if (myq < N) {
-    uint16_t* orow = O + base + (size_t)myq * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
-                   pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
+        for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
+        return;
       }
-    if (g == 0) LSE[(size_t)bh * N + myq] = ltot > 0.f ? (m + log2_hw(ltot)) * kLn2 : -INFINITY;
+      const int lim = MASK ? (CAUSAL ? min(myq, N - 1) : N - 1) - i * PP_BK - 4 * g : 0;
+      softmax_inplace128<MASK>(s, oacc, m, lsum, c, lim);
+    };
+    // Group 0's pair k up to its first barrier: the loads, then matrix phase
+    // k (P(k-1) V(k-1), then S(k)), if `mat`.
+    auto g0_pair = [&](int k, auto qk_tag, auto pv_tag, bool mat) {
+      pp_load_matrix<decltype(qk_tag)::value, decltype(pv_tag)::value>(
+          kslot(k), vslot(k - 1), kslot(k + 1), vslot(k), k + 1 < ntiles, k < ntiles, mat, dma, K + base, V + base, N,
+          (k + 1) * PP_BK, k * PP_BK, wave, qf, s, oacc, lane);
+    };
+    // Group 1's pair k up to its second barrier: the loads, softmax phase
+    // k-1 (sm), the barrier, then matrix phase k if `mat`.
+    auto g1_pair = [&](int k, auto qk_tag, auto pv_tag, bool mat, auto&& sm) {
+      pp_load_softmax_matrix<decltype(qk_tag)::value, decltype(pv_tag)::value>(
+          kslot(k), vslot(k - 1), kslot(k + 1), vslot(k), k + 1 < ntiles, k < ntiles, mat, dma, K + base, V + base, N,
+          (k + 1) * PP_BK, k * PP_BK, wave, qf, s, oacc, lane, sm);
+    };
+    // The last matrix phase: P(ntiles-1) V(ntiles-1) only, no loads before it.
+    auto matrix = [&](int k, auto qk_tag, auto pv_tag) {
+      pp_matrix<decltype(qk_tag)::value, decltype(pv_tag)::value>(kslot(k), vslot(k - 1), qf, s, oacc, lane);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+
+    dma.k_tile(K + base, N, 0, kslot(0), wave);
+    wait_vmem();
+    pp_sync();
+
+    // In the pairs whose softmax needs the mask (the causal diagonal, the
+    // ragged end of N) a wave skips matrix phase k when neither tile k nor
+    // tile k-1 holds a key it sees (P(k-1) is then zero and S(k) unused);
+    // the barriers stay the same for every wave.
+    const int k_mask = max(1, min(grp == 0 ? first_mask_w : first_mask_w + 1, ntiles));
+    if (grp == 0) {
+      g0_pair(0, T{}, F{}, true);
+      pp_sync();
+      if (0 < first_mask_w) softmax(0, F{}); else softmax(0, T{});
+      wait_vmem();
+      pp_sync();
+      int k = 1;
+      for (; k < k_mask; ++k) {
+        g0_pair(k, T{}, T{}, true);
+        pp_sync();
+        softmax(k, F{});
+        wait_vmem();
+        pp_sync();
+      }
+      for (; k < ntiles; ++k) {
+        g0_pair(k, T{}, T{}, k - 1 <= last_w);
+        pp_sync();
+        softmax(k, T{});
+        wait_vmem();
+        pp_sync();
+      }
+      if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
+      pp_sync();
+      pp_sync();
+    } else {
+      g1_pair(0, T{}, F{}, true, [] {});
+      wait_vmem();
+      pp_sync();
+      int k = 1;
+      for (; k < k_mask; ++k) {
+        g1_pair(k, T{}, T{}, true, [&] { softmax(k - 1, F{}); });
+        wait_vmem();
+        pp_sync();
+      }
+      for (; k < ntiles; ++k) {
+        g1_pair(k, T{}, T{}, k - 1 <= last_w, [&] { softmax(k - 1, T{}); });
+        wait_vmem();
+        pp_sync();
+      }
+      if (ntiles - 1 < first_mask_w) softmax(ntiles - 1, F{}); else softmax(ntiles - 1, T{});
+      pp_sync();
+      if (ntiles - 1 <= last_w) matrix(ntiles, F{}, T{});
+      pp_sync();
+    }
+
+    const float ltot = sum_halves(lsum);
+    const float inv = ltot > 0.f ? rcp_hw(ltot) : 0.f;
+    if (myq < N) {
+      uint16_t* orow = O + base + (size_t)myq * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 w = {pack_bf16x2(oacc[db][4 * a] * inv, oacc[db][4 * a + 1] * inv),
+                     pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * a + 4 * g) = w;
+        }
+      if (g == 0) LSE[(size_t)bh * N + myq] = ltot > 0.f ? (m + log2_hw(ltot)) * kLn2 : -INFINITY;
+    }
   }
+}
+
+// Workgroups of the persistent forward: one per compute unit, at most one
+// per item.
+inline int persistent_grid(long long items) {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
+  }
+  return (int)(items < ncu ? items : ncu);
 }
 
 template <int D, bool CAUSAL, bool SPARSE = false>
@@ -696,8 +819,14 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
       const int nqb = (N + PP_BR - 1) / PP_BR;
       const long long total = (long long)BH * nqb;
       if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)total), dim3(PP_NT), 0, stream, q, k, v, o, lse, N,
-                         nqb, (int)total, score_coef(scale));
+#ifdef FA_FWD_PERSIST
+      const int grid = persistent_grid(total);
+      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL, true>), dim3((unsigned)grid), dim3(PP_NT), 0, stream, q, k, v, o,
+                         lse, N, nqb, BH, score_coef(scale));
+#else
+      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL, false>), dim3((unsigned)total), dim3(PP_NT), 0, stream, q, k, v, o,
+                         lse, N, nqb, BH, score_coef(scale));
+#endif
       return hipGetLastError();
     }
   }

@@ -99,18 +99,32 @@ def test_block_sparse_all_hidden(fa, N):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_all_visible_equals_dense_bitwise(fa, d, causal):
+    """With every block visible the block-sparse kernel does the dense
+    kernel's arithmetic tile by tile: bit-identical to fa_forward wherever
+    fa_forward runs the same kernel family (d = 64, and causal d = 128 up to
+    N = 2048); the d = 128 non-causal forward runs the two-group kernel (its
+    lazy rescale decides per 128 keys), so there both are compared with the
+    oracle."""
     import torch
 
     N = 777
     nb = -(-N // BLK)
-    q, k, v = (dev(a) for a in random_inputs(4, (2, 3, N, d), "bf16", 3))
+    qh, kh, vh = random_inputs(4, (2, 3, N, d), "bf16", 3)
+    q, k, v = dev(qh), dev(kh), dev(vh)
     od, ld = fa.forward(q, k, v, causal=causal)
+    same_kernel = d == 64 or causal
+    ref = None if same_kernel else oracle.attention_forward(*(fi.exact_f64(a) for a in (qh, kh, vh)), causal,
+                                                            d ** -0.5)
     for balance in (False, True):   # every row has the same count: nothing is split either way
         o, lse = fa.forward_block_sparse(q, k, v, _mask_dev(np.ones((nb, nb), np.uint8)), causal=causal,
                                          balance=balance)
         torch.cuda.synchronize()
-        assert torch.equal(o.view(torch.int16), od.view(torch.int16))
-        assert torch.equal(lse, ld)
+        if same_kernel:
+            assert torch.equal(o.view(torch.int16), od.view(torch.int16))
+            assert torch.equal(lse, ld)
+        else:
+            for oo, ll in ((o, lse), (od, ld)):
+                assert max_abs(host64(oo), ref[0]) <= 2e-2 and max_abs(host64(ll), ref[1]) <= 1e-3
 
 
 def test_block_diagonal_equals_independent_segments(fa):

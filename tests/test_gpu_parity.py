@@ -92,19 +92,19 @@ def test_bf16_forward_causal_above_2048(fa, N):
     _check_fwd(fa, "bf16", 1, 2, N, 128, True, seed=N)
 
 
-@pytest.mark.parametrize("N", [2049, 2300])
-def test_two_group_forward_equals_one_group_rows(fa, N):
-    """Per query the two-group kernel does the one-group kernel's arithmetic
-    in the same order, so the first 2048 queries of a causal N > 2048
-    problem (which see only the first 2048 keys) are bit-identical to the
-    causal N = 2048 problem on the same rows."""
+@pytest.mark.parametrize("N", [2305, 2500])
+def test_two_group_forward_rows_independent_of_n(fa, N):
+    """The two-group kernel computes each query row from the keys it sees, in
+    the same tile order whatever N is: the first 2304 rows of a causal
+    problem with N > 2304 are bit-identical to the causal N = 2304 problem on
+    the same rows (both run the two-group kernel)."""
     import torch
 
     q, k, v = random_inputs(7, (1, 2, N, 128), "bf16", 3)
     o1, l1 = _run_fwd(fa, q, k, v, True, 128 ** -0.5)
-    o2, l2 = _run_fwd(fa, q[:, :, :2048].copy(), k[:, :, :2048].copy(), v[:, :, :2048].copy(), True, 128 ** -0.5)
-    assert torch.equal(o1[:, :, :2048].view(torch.int16), o2.view(torch.int16))
-    assert torch.equal(l1[:, :, :2048], l2)
+    o2, l2 = _run_fwd(fa, q[:, :, :2304].copy(), k[:, :, :2304].copy(), v[:, :, :2304].copy(), True, 128 ** -0.5)
+    assert torch.equal(o1[:, :, :2304].view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1[:, :, :2304], l2)
 
 
 @pytest.mark.parametrize("causal", [False, True])
