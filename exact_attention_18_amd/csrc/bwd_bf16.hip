@@ -274,22 +274,33 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     if (wave == 2) reinterpret_cast<float*>(stage + 2 * L::TILE)[lane] = __uint_as_float(lse_bits) * kLog2e;
   };
 
-  fetch(qstart, smem + L::V_ELEMS);
+  // Query tiles are visited from the last one down to the diagonal, so
+  // that the workgroups of one head (all key blocks) start on the same tile
+  // and read the same Q and dO tiles at about the same time, each stopping
+  // at its own diagonal: the tiles are fetched once into L2 and shared,
+  // rather than streamed by each block from a different start.
+#ifdef FA_BWD_ASC
+  auto tile_of = [&](int p) { return p; };
+#else
+  auto tile_of = [&](int p) { return ntiles - 1 - p; };
+#endif
+  fetch(qstart + tile_of(0) * Q_TILE, smem + L::V_ELEMS);
   vrows.template store<L::VS>(Vs, tid);
   put_lse(smem + L::V_ELEMS);
   wait_vmem();
   __syncthreads();
 
-  // One query tile for this wave.  MASK: the tile may straddle the diagonal
-  // of this wave's keys (some query < some key).
-  auto step = [&](int i, auto mask_tag) {
+  // Query tile i, the p-th one visited, for this wave.  MASK: the tile may
+  // straddle the diagonal of this wave's keys (some query < some key).
+  auto step = [&](int p, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    const int i = tile_of(p);
     const int qt0 = qstart + i * Q_TILE;
-    const uint16_t* Qs = smem + L::V_ELEMS + (i & 1) * L::STAGE;
+    const uint16_t* Qs = smem + L::V_ELEMS + (p & 1) * L::STAGE;
     const uint16_t* Gs = Qs + L::TILE;
     const float* lse2 = reinterpret_cast<const float*>(Qs + 2 * L::TILE);   // LSE * log2(e)
     const float* dls = lse2 + 64;
-    if (i + 1 < ntiles) fetch(qt0 + Q_TILE, smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
+    if (p + 1 < ntiles) fetch(qstart + tile_of(p + 1) * Q_TILE, smem + L::V_ELEMS + ((p + 1) & 1) * L::STAGE);
 
     if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
       // S and dP: element r is query qt0 + qrow(r) + g, key myk.  At
@@ -364,16 +375,22 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         __builtin_amdgcn_sched_group_barrier(0x008, AH / 2, 0);
       }
     }
-    if (i + 1 < ntiles) put_lse(smem + L::V_ELEMS + ((i + 1) & 1) * L::STAGE);
+    if (p + 1 < ntiles) put_lse(smem + L::V_ELEMS + ((p + 1) & 1) * L::STAGE);
     wait_vmem();
     __syncthreads();
   };
   // Causal: the first KV_BLK / Q_TILE tiles straddle the diagonals of the
   // workgroup's waves; every later tile is fully visible.
-  int i = 0;
-  if (CAUSAL)
-    for (; i < min(ntiles, KV_BLK / Q_TILE); ++i) step(i, std::true_type{});
-  for (; i < ntiles; ++i) step(i, std::false_type{});
+  const int n_diag = CAUSAL ? min(ntiles, KV_BLK / Q_TILE) : 0;
+#ifdef FA_BWD_ASC
+  int p = 0;
+  for (; p < n_diag; ++p) step(p, std::true_type{});
+  for (; p < ntiles; ++p) step(p, std::false_type{});
+#else
+  int p = 0;
+  for (; p < ntiles - n_diag; ++p) step(p, std::false_type{});
+  for (; p < ntiles; ++p) step(p, std::true_type{});
+#endif
 
   if (myk < N) {
     store_acc_row<D>(dK + base + (size_t)myk * D, dkt, scale, g);

@@ -488,14 +488,10 @@ __device__ __forceinline__ void softmax_inplace128(f32x16 (&s)[4], f32x16 (&oacc
 // tiles.  P(k-1) V(k-1) goes first so that P's registers (which are S's,
 // see softmax_inplace128) are free before S(k) is written.
 //
-// Work items are (batch*head, 256-query block) pairs, heaviest first when
-// the mask makes the work grow with the block index; when B*H is a multiple
-// of 8 the workgroups of each XCD (id % 8) take only the heads h with h % 8
-// equal to their XCD, so a head's K and V are read through one L2.  With
-// PERSIST (not built by default: the loop's extra live values do not fit the
-// register budget), one workgroup per compute unit walks a list of items
-// dealt in a serpentine (round t to workgroups 0, 1, ... when t is even and
-// in the reverse order when t is odd).
+// One workgroup per (batch*head, 256-query block), dispatched heaviest
+// first when the mask makes the work grow with the block index; when B*H is
+// a multiple of 8 the workgroups of each XCD (id % 8) take only the heads h
+// with h % 8 equal to their XCD, so a head's K and V are read through one L2.
 constexpr int PP_BK = 128;   // keys per tile
 
 struct PpLds {
@@ -635,7 +631,7 @@ __device__ __forceinline__ void pp_load_softmax_matrix(const uint16_t* __restric
   if (mat) pp_matrix<QK, PV>(Kr, Vr, qf, s, oacc, lane);
 }
 
-template <bool CAUSAL, bool PERSIST>
+template <bool CAUSAL>
 __global__ void __launch_bounds__(PP_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int nqb, int BH, float c) {
@@ -649,17 +645,14 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
   const int grp = wave >> 2;
   const int g = lane >> 5, l32 = lane & 31;
 
-  // item list of this workgroup (see above)
-  const int G = gridDim.x;
-  const int nx = (BH % 8 == 0 && G % 8 == 0) ? 8 : 1;
-  const int xg = blockIdx.x % nx, wl = blockIdx.x / nx, GL = G / nx;
-  const int hx = BH / nx, count = hx * nqb;
+  // this workgroup's item (see above)
+  const int nx = BH % 8 == 0 ? 8 : 1;
+  const int xg = blockIdx.x % nx, r = blockIdx.x / nx;
+  const int hx = BH / nx;
   PpDma dma;
   dma.init(wave, lane);
 
-  for (int t = 0; PERSIST || t < 1; ++t) {
-    const int r = t * GL + ((t & 1) ? GL - 1 - wl : wl);
-    if (r >= count) break;
+  {
     const int hl = CAUSAL ? r % hx : r / nqb;
     const int qb = CAUSAL ? nqb - 1 - r / hx : r % nqb;
     const int bh = hl * nx + xg;
@@ -798,17 +791,6 @@ fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, co
   }
 }
 
-// Workgroups of the persistent forward: one per compute unit, at most one
-// per item.
-inline int persistent_grid(long long items) {
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
-  }
-  return (int)(items < ncu ? items : ncu);
-}
-
 template <int D, bool CAUSAL, bool SPARSE = false>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                   int BH, int N, float scale, hipStream_t stream, const uint8_t* bmask = nullptr) {
@@ -819,14 +801,8 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint1
       const int nqb = (N + PP_BR - 1) / PP_BR;
       const long long total = (long long)BH * nqb;
       if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-#ifdef FA_FWD_PERSIST
-      const int grid = persistent_grid(total);
-      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL, true>), dim3((unsigned)grid), dim3(PP_NT), 0, stream, q, k, v, o,
-                         lse, N, nqb, BH, score_coef(scale));
-#else
-      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL, false>), dim3((unsigned)total), dim3(PP_NT), 0, stream, q, k, v, o,
-                         lse, N, nqb, BH, score_coef(scale));
-#endif
+      hipLaunchKernelGGL((fwd_pp_kernel<CAUSAL>), dim3((unsigned)total), dim3(PP_NT), 0, stream, q, k, v, o, lse, N,
+                         nqb, BH, score_coef(scale));
       return hipGetLastError();
     }
   }
