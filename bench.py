@@ -15,7 +15,10 @@ the whole step's FLOPs over its wall time between two synchronisations.
 Each kernel is also bracketed by HIP events on the launch stream; the kernel
 with the largest average duration is reported with its roofline:
 achieved = its algorithmic FLOPs per launch / its average duration, against
-the MI355X dense bf16 matrix-core peak.
+the MI355X dense bf16 matrix-core peak.  Beside it, the vendor bf16 GEMM
+(torch.matmul on 8192-square operands) is timed in the same run: under
+sustained matrix-core load the chip does not hold its 2.4 GHz clock, and
+that GEMM shows what dense bf16 work reaches at the clock it does hold.
 
 Timing series (page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の
 実践的エンジニアリング", section 「推論レイテンシとスループットの測定方法」: CUDA events
@@ -56,6 +59,7 @@ FP8_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal", "bf
 EXTRA_BWD = ["bf16_b16h32n1024d64_causal_fwdbwd"]
 SERIES_N = 20          # launches per timing series
 FLUSH_MIB = 512        # scratch written before each launch of the flushed series
+GEMM_REF_N = 8192      # square bf16 GEMM timed as the dense matrix-core reference
 
 
 def _products(w, n):
@@ -438,6 +442,17 @@ def main():
                            "tflops": round(dw.flops() / (dms * 1e-3) / 1e12, 2)})
             del dq_, dk_, dv_, do_, dl_, dws
 
+    # Reference for what dense bf16 matrix-core work reaches on this GPU at
+    # the clocks it holds under load: the vendor GEMM (torch.matmul, i.e.
+    # hipBLASLt) on square 8192 operands, timed the same way.
+    ga_ = torch.randn(GEMM_REF_N, GEMM_REF_N, device=dev, dtype=torch.bfloat16)
+    gb_ = torch.randn(GEMM_REF_N, GEMM_REF_N, device=dev, dtype=torch.bfloat16)
+    gemm_ms = series(lambda: torch.matmul(ga_, gb_), False)["median_ms"]
+    gemm_tf = 2.0 * GEMM_REF_N ** 3 / (gemm_ms * 1e-3) / 1e12
+    gemm_ref = {"op": f"torch.matmul bf16 {GEMM_REF_N}x{GEMM_REF_N}x{GEMM_REF_N} (hipBLASLt)",
+                "median_ms": round(gemm_ms, 4), "tflops": round(gemm_tf, 1),
+                "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)}
+    del ga_, gb_
     del flush_buf
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
@@ -452,7 +467,9 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom[0], w.name),
-                "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4)}
+                "flop_per_launch": dom[2], "avg_ms": round(dom_ms, 4),
+                "library_gemm_tflops": gemm_ref["tflops"],
+                "frac_of_library_gemm": round(achieved / gemm_ref["tflops"], 4)}
     if mfma:
         # the matrix-core work the counters saw (recomputed products
         # included) over this run's launch time, and the busy fraction
@@ -485,6 +502,7 @@ def main():
         "kernels": kernel_table,
         "series": {"launches": SERIES_N, "flush_MiB": FLUSH_MIB, "step": step_series,
                    "fa_backward": backward_series},
+        "gemm_reference": gemm_ref,
         "headline_forward": headline,
         "backward_d64": extra_backward,
         "block_sparse_forward": block_sparse,
