@@ -25,7 +25,7 @@ Timing series (page "Flash Attention 2で打破するローカルLLMの「メモ
 around repeated launches after warm-up): the step and every secondary
 workload are also launched SERIES_N times, each launch bracketed by its own
 pair of HIP events, and reported as the median and the minimum; a second
-series writes a 512 MiB scratch buffer before every launch, which evicts the
+series reads a 512 MiB scratch buffer before every launch, which evicts the
 L2 caches and the MALL, so that no input starts out on chip.
 
 cpu_baseline: the fp64 oracle (materialising S and P) timed on the host on
@@ -58,7 +58,7 @@ HEADLINE_FWD = ["bf16_b16h32n1024d64", "bf16_b16h32n1024d64_causal", "bf16_b4h16
 FP8_FWD = ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal", "bf16_b1h16n16384d128"]
 EXTRA_BWD = ["bf16_b16h32n1024d64_causal_fwdbwd"]
 SERIES_N = 20          # launches per timing series
-FLUSH_MIB = 512        # scratch written before each launch of the flushed series
+FLUSH_MIB = 512        # scratch read before each launch of the flushed series
 GEMM_REF_N = 8192      # square bf16 GEMM timed as the dense matrix-core reference
 
 
@@ -293,17 +293,20 @@ def main():
                         "tflops": round(f / (per_kernel_ms[n] * 1e-3) / 1e12, 1) if f else None}
                     for n, _, f in kernels}
 
-    flush_buf = torch.empty(FLUSH_MIB * 2**20, dtype=torch.uint8, device=dev)
-    flush_val = [0]
+    # The flush reads the scratch buffer (a reduction into one value): a read
+    # evicts L2 and MALL lines as a write does, but leaves no dirty lines
+    # whose write-back would fall into the timed launch (writing the buffer
+    # instead made the decode launch after it 25% slower).
+    flush_buf = torch.zeros(FLUSH_MIB * 2**20 // 4, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
 
     def flush():
-        flush_val[0] = (flush_val[0] + 1) & 0xFF
-        flush_buf.fill_(flush_val[0])
+        torch.sum(flush_buf, dim=0, dtype=torch.int64, out=flush_out)
 
     def series(fn, flushed, n=SERIES_N, warm=3):
         """HIP-event times (ms) of ``fn`` launched ``n`` times on ``stream``,
         each launch bracketed by its own events (after a short untimed burst
-        that brings the clocks back up); ``flushed`` writes the scratch buffer
+        that brings the clocks back up); ``flushed`` reads the scratch buffer
         before every launch.  Returns median, minimum and mean."""
         clock_warm(fn, CLOCK_REWARM_S)
         for _ in range(warm):
