@@ -274,16 +274,15 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     if (wave == 2) reinterpret_cast<float*>(stage + 2 * L::TILE)[lane] = __uint_as_float(lse_bits) * kLog2e;
   };
 
-  // Query tiles are visited from the last one down to the diagonal, so
-  // that the workgroups of one head (all key blocks) start on the same tile
-  // and read the same Q and dO tiles at about the same time, each stopping
-  // at its own diagonal: the tiles are fetched once into L2 and shared,
-  // rather than streamed by each block from a different start.
-#ifdef FA_BWD_ASC
-  auto tile_of = [&](int p) { return p; };
-#else
-  auto tile_of = [&](int p) { return ntiles - 1 - p; };
-#endif
+  // With the causal mask, query tiles are visited from the last one down to
+  // the diagonal, so that the workgroups of one head (all key blocks) start
+  // on the same tile and read the same Q and dO tiles at about the same
+  // time, each stopping at its own diagonal: the tiles are fetched once into
+  // L2 and shared, rather than streamed by each block from a different
+  // start.  Without the mask every block visits every tile, so the order does not
+  // change what is shared; the ascending order then compiles without
+  // spilling at d = 128 (the descending one spilled 12-16 bytes per lane).
+  auto tile_of = [&](int p) { return CAUSAL ? ntiles - 1 - p : p; };
   fetch(qstart + tile_of(0) * Q_TILE, smem + L::V_ELEMS);
   vrows.template store<L::VS>(Vs, tid);
   put_lse(smem + L::V_ELEMS);
@@ -382,15 +381,9 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   // Causal: the first KV_BLK / Q_TILE tiles straddle the diagonals of the
   // workgroup's waves; every later tile is fully visible.
   const int n_diag = CAUSAL ? min(ntiles, KV_BLK / Q_TILE) : 0;
-#ifdef FA_BWD_ASC
-  int p = 0;
-  for (; p < n_diag; ++p) step(p, std::true_type{});
-  for (; p < ntiles; ++p) step(p, std::false_type{});
-#else
   int p = 0;
   for (; p < ntiles - n_diag; ++p) step(p, std::false_type{});
   for (; p < ntiles; ++p) step(p, std::true_type{});
-#endif
 
   if (myk < N) {
     store_acc_row<D>(dK + base + (size_t)myk * D, dkt, scale, g);
