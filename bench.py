@@ -159,7 +159,19 @@ def cpu_baseline(w, budget_s: float):
             break
     dt = time.perf_counter() - t0
     per_head = (w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)) / (w.B * w.H)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in pools
+                             if i.get("user_api") == "blas"})) or "unknown"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": per_head * done / dt / 1e12,
         "unit": "TFLOP/s",
@@ -167,6 +179,8 @@ def cpu_baseline(w, budget_s: float):
         "kind": "oracle",
         "sample": f"{done} of {w.B * w.H} (batch, head) pairs, forward{'+backward' if w.backward else ''}, "
                   f"fp64 numpy, {dt:.1f} s, host nproc {os.cpu_count()}",
+        "cpu_model": cpu_model,
+        "blas": blas,
     }
 
 
