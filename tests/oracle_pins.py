@@ -523,8 +523,65 @@ def fp8_pin_failures(fp8) -> list[str]:
     e_rot = np.sqrt(np.mean((fp8.attention_forward_fp8(qo, ko, vo, sg, False, d ** -0.5)[0] - ref) ** 2))
     if not e_rot * 2.0 < e_plain:
         fails.append("rotation_lowers_outlier_error")
+    fails += _scale_granularity_failures(fp8, r)
 
     fails += _p_bound_failures(fp8, r)
+    return fails
+
+
+def _scale_granularity_failures(fp8, r) -> list[str]:
+    """Why the rotation's gain depends on where the outliers sit, not on how
+    finely the scales are set.  E4M3 is a floating-point format, so above its
+    subnormal range an element's relative rounding error does not depend on
+    the scale: one power-of-two scale for the whole tensor (the setting with
+    the fewest scales) and one per 32 elements give the same quantised
+    values here, hence the same error with and without the rotation.  What
+    the rotation changes is how the error of q.k is spread over the
+    products q_i k_i.  Outliers that sit in the same channels of Q and K
+    make a few products dominate that error, and the rotation spreads them
+    (gain well above 2x).  Isolated outlier entries rarely meet a large
+    partner, so the gain stays small (below 2x).  The per-tensor quantiser
+    is built here from the pinned codec and block exponent."""
+    fails = []
+
+    def per_tensor(x):
+        t = fp8.block_exponent(np.abs(x).max())
+        return fp8.e4m3_decode(fp8.e4m3_encode(x / np.float32(2.0 ** t))) * 2.0 ** t
+
+    def per_block(x):
+        c, t = fp8.quantize_rows(x)
+        return fp8._dequant_rows(c, t)
+
+    def attn(q, k, v, sc):
+        sm = sc * (q.astype(np.float64) @ k.astype(np.float64).T)
+        sm = np.exp(sm - sm.max(axis=1, keepdims=True))
+        return (sm / sm.sum(axis=1, keepdims=True)) @ v
+
+    d, n = 128, 256
+    gains = {}
+    for kind in ("channels", "isolated"):
+        q, k, v = (r.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+        if kind == "channels":
+            ch = r.choice(d, 2, replace=False)
+            q[:, ch] *= 10.0
+            k[:, ch] *= 10.0
+        else:
+            for a in (q, k):
+                a[r.random(a.shape) < 0.001] *= 10.0
+        sg = np.where(r.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+        qr, kr = fp8.fwht_f32(q * sg), fp8.fwht_f32(k * sg)
+        ref = attn(q, k, v.astype(np.float64), d ** -0.5)
+        for name, qz in (("tensor", per_tensor), ("block", per_block)):
+            e_plain = np.sqrt(np.mean((attn(qz(q), qz(k), v, d ** -0.5) - ref) ** 2))
+            e_rot = np.sqrt(np.mean((attn(qz(qr), qz(kr), v, d ** -0.5 / d) - ref) ** 2))
+            gains[(kind, name)] = e_plain / e_rot
+    for kind in ("channels", "isolated"):
+        if abs(gains[(kind, "tensor")] - gains[(kind, "block")]) > 0.02 * gains[(kind, "block")]:
+            fails.append(f"scale_granularity_changes_gain:{kind}")
+    if not gains[("channels", "tensor")] > 2.0:
+        fails.append("channel_outlier_gain")
+    if not 1.0 < gains[("isolated", "tensor")] < 2.0:
+        fails.append("isolated_outlier_gain")
     return fails
 
 
