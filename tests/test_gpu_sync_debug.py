@@ -1,0 +1,60 @@
+"""FA_SYNC_DEBUG=1: every entry point synchronises its stream before it
+returns and reports a kernel's own failure as FA_ERR_HIP.  With correct
+inputs the calls must still return FA_OK and give the same bits as without
+it (the kernels and launches are the same; only the host waits)."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+from tests.gpu_util import dev, random_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_18_amd as fa
+
+    fa._lib.load()
+    return fa
+
+
+def _run_all(fa):
+    """Forward, backward, decode, block-sparse and FP8 on small ragged shapes;
+    returns every output as a host array."""
+    import torch
+
+    out = []
+    B, H, N, d = 2, 3, 300, 128
+    q, k, v, do = (dev(a) for a in random_inputs(3, (B, H, N, d), "bf16", 4))
+    o, lse = fa.forward(q, k, v, causal=True)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, causal=True)
+    qd, kd, vd = (dev(a) for a in random_inputs(4, (B, H, 3, d), "bf16", 1) + random_inputs(5, (B, H, 777, d), "bf16", 2))
+    od, ld = fa.decode(qd, kd, vd, causal=True)
+    nqb = (N + 127) // 128
+    mask = torch.from_numpy(fi.random_block_mask(6, nqb, 0.5)).to(q.device)
+    ob, lb = fa.forward_block_sparse(q, k, v, mask)
+    o8, l8 = fa.forward_fp8(q, k, v, dev(fi.random_signs(0, d)))
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv, od, ld, ob, lb, o8, l8):
+        out.append(t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy())
+    return out
+
+
+def test_sync_debug_same_results(fa):
+    os.environ.pop("FA_SYNC_DEBUG", None)
+    ref = _run_all(fa)
+    os.environ["FA_SYNC_DEBUG"] = "1"
+    try:
+        got = _run_all(fa)
+    finally:
+        os.environ.pop("FA_SYNC_DEBUG", None)
+    for a, b in zip(ref, got):
+        assert np.array_equal(a, b, equal_nan=True)
