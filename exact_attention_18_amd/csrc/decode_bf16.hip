@@ -232,17 +232,19 @@ hipError_t launch_split_nq(const uint16_t* q, const uint16_t* k, const uint16_t*
 
 DecodeSplit decode_split(long long BH, int nq, int Nk, int d) {
   // Keys per chunk: a multiple of 64 (a whole number of steps for every
-  // instantiation) sized for about 2048 chunk wavefronts in all (two per
-  // SIMD), or 1024 (one per SIMD) for a single query, all resident at once,
-  // each streaming one long contiguous range.  Measured on MI355X, fewer
-  // longer streams beat more shorter ones (16k chunks of 128 keys ran 25%
-  // slower on the B=8 H=16 Nk=16384 d=128 decode), and even one (batch,
-  // head) still fills the 256 compute units.  With one query a wave keeps 32
-  // loads in flight and does little arithmetic per key, so one wave per SIMD
-  // streams faster (+4-13%); with two or more queries the arithmetic needs
-  // the second wave to overlap it (1024 chunks ran 25% slower at nq = 2).
+  // instantiation) sized for a number of chunk wavefronts that all stay
+  // resident, each streaming one long contiguous range: 1024 (one per SIMD)
+  // for one query, 2048 for two, 3072 for three or four, 2048 for five to
+  // eight.  Measured on MI355X, fewer longer streams beat more shorter ones
+  // (16k chunks of 128 keys ran 25% slower on the B=8 H=16 Nk=16384 d=128
+  // decode), and even one (batch, head) still fills the 256 compute units.
+  // With one query a wave keeps 32 loads in flight and does little
+  // arithmetic per key, so one wave per SIMD streams fastest (+4-13%); more
+  // queries need more waves to overlap their arithmetic (1024 chunks ran
+  // 25% slower at nq = 2; 3072 ran 14-15% faster than 2048 at nq = 3-4 and
+  // 4-7% slower at nq = 6-8).
   DecodeSplit r;
-  const long long target = nq == 1 ? 1024 : 2048;
+  const long long target = nq == 1 ? 1024 : nq <= 2 ? 2048 : nq <= 4 ? 3072 : 2048;
   long long chunk = (BH * (long long)Nk + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
