@@ -470,6 +470,26 @@ def main():
                 "median_ms": round(gemm_ms, 4), "tflops": round(gemm_tf, 1),
                 "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)}
     del ga_, gb_
+    # The same for FP8 (OCP E4M3, the format of the FP8 path), through
+    # torch._scaled_mm with unit scales; left out where this torch build has
+    # no such kernel.
+    gemm_ref_fp8 = None
+    try:
+        fa_ = torch.randn(GEMM_REF_N, GEMM_REF_N, device=dev).to(torch.float8_e4m3fn)
+        fb_ = torch.randn(GEMM_REF_N, GEMM_REF_N, device=dev).to(torch.float8_e4m3fn).t()
+        one_ = torch.ones((), device=dev)
+        f8ms = series(lambda: torch._scaled_mm(fa_, fb_, scale_a=one_, scale_b=one_, out_dtype=torch.bfloat16),
+                      False)["median_ms"]
+        f8tf = 2.0 * GEMM_REF_N ** 3 / (f8ms * 1e-3) / 1e12
+        gemm_ref_fp8 = {"op": f"torch._scaled_mm fp8 e4m3 {GEMM_REF_N}x{GEMM_REF_N}x{GEMM_REF_N} (hipBLASLt)",
+                        "median_ms": round(f8ms, 4), "tflops": round(f8tf, 1),
+                        "frac_of_peak": round(f8tf / PEAK_FP8_TFLOPS, 4)}
+        del fa_, fb_
+    except (RuntimeError, AttributeError, TypeError):
+        pass
+    if gemm_ref_fp8:
+        for e in fp8:
+            e["frac_of_library_fp8_gemm"] = round(e["tflops"] / gemm_ref_fp8["tflops"], 4)
     del flush_buf
     if args.copy_calibration:
         copy_calibration(dev, args.copy_calibration, 3)
@@ -520,6 +540,7 @@ def main():
         "series": {"launches": SERIES_N, "flush_MiB": FLUSH_MIB, "step": step_series,
                    "fa_backward": backward_series},
         "gemm_reference": gemm_ref,
+        "gemm_reference_fp8": gemm_ref_fp8,
         "headline_forward": headline,
         "backward_d64": extra_backward,
         "block_sparse_forward": block_sparse,
