@@ -9,7 +9,7 @@
 //    FlashAttention-2, on 64-wide waves);
 //  * K/V tiles of 64 keys stream through a double-buffered LDS stage; tile j+1
 //    is fetched by direct HBM-to-LDS loads while tile j is computed (the
-//    two-group kernel below stages its tiles through registers);
+//    two-group kernel below does the same with 128-key tiles);
 //  * S^T = K Q^T and O^T += V^T P^T on the bf16 matrix cores.  Computing the
 //    transposed products puts one query per lane (two lanes per query), so
 //    the row max, the row sum and the output rescale are per-lane values.
