@@ -311,11 +311,11 @@ def main():
     # evicts L2 and MALL lines as a write does, but leaves no dirty lines
     # whose write-back would fall into the timed launch (writing the buffer
     # instead made the decode launch after it 25% slower).
-    flush_buf = torch.zeros(FLUSH_MIB * 2**20 // 4, dtype=torch.int32, device=dev)
-    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+    flush_buf = torch.zeros(FLUSH_MIB * 2**20 // 4, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
     def flush():
-        torch.sum(flush_buf, dim=0, dtype=torch.int64, out=flush_out)
+        torch.sum(flush_buf, dim=0, out=flush_out)
 
     def series(fn, flushed, n=SERIES_N, warm=3):
         """HIP-event times (ms) of ``fn`` launched ``n`` times on ``stream``,
