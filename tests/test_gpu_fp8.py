@@ -171,18 +171,21 @@ def test_rotation_lowers_outlier_error(fa):
     assert e_rot < e_plain
 
 
-def test_full_size_fp8(fa):
-    """The B=4 H=16 N=4096 d=128 causal workload (inputs x0.5) through the FP8
-    path: sampled rows of sampled heads against the oracle's FP8 attention,
-    and against exact attention for context; repeat launches bit-identical."""
+@pytest.mark.parametrize("name", ["bf16_b4h16n4096d128_causal_x0.5", "bf16_b1h16n16384d128_causal",
+                                  "bf16_b1h16n16384d128"])
+def test_full_size_fp8(fa, name):
+    """The d=128 workloads the benchmark times through the FP8 path (N=4096
+    causal with inputs x0.5, N=16384 causal and non-causal): sampled rows of
+    sampled heads against the oracle's FP8 attention, and against exact
+    attention for context; repeat launches bit-identical."""
     import torch
 
-    w = fi.WORKLOADS["bf16_b4h16n4096d128_causal_x0.5"]
+    w = fi.WORKLOADS[name]
     x = fi.make_inputs(w, with_grad=False)
     tq, tk, tv = dev(x["q"]), dev(x["k"]), dev(x["v"])
     signs = _signs_dev(0)
-    o, lse = fa.forward_fp8(tq, tk, tv, signs, causal=True, scale=w.scale)
-    o2, lse2 = fa.forward_fp8(tq, tk, tv, signs, causal=True, scale=w.scale)
+    o, lse = fa.forward_fp8(tq, tk, tv, signs, causal=w.causal, scale=w.scale)
+    o2, lse2 = fa.forward_fp8(tq, tk, tv, signs, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
@@ -193,13 +196,13 @@ def test_full_size_fp8(fa):
     for (b, h) in sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}):
         rows = np.unique(np.concatenate([[0, 1, 63, 64, w.N - 1], rng.choice(w.N, 40, replace=False)]))
         qh, kh, vh = (fi.exact_f64(x[n][b, h]) for n in ("q", "k", "v"))
-        ro, rl, bound = ofp8.attention_forward_fp8_rows(qh, kh, vh, rows, sg, True, w.scale)
+        ro, rl, bound = ofp8.attention_forward_fp8_rows(qh, kh, vh, rows, sg, w.causal, w.scale)
         tol = 2.0 ** -4 * bound + 2.0 ** -8 * np.abs(ro) + 1e-4
         assert np.all(np.abs(oh[b, h, rows] - ro) <= tol)
         assert np.abs(lh[b, h, rows] - rl).max() <= 1e-3
-        ex, _ = attention_forward_rows(qh, kh, vh, rows, True, w.scale)
+        ex, _ = attention_forward_rows(qh, kh, vh, rows, w.causal, w.scale)
         worst_exact = max(worst_exact, float(np.abs(oh[b, h, rows] - ex).max()))
-    print(f"FP8 max |O - exact| on sampled rows: {worst_exact:.4g}")
+    print(f"FP8 {name}: max |O - exact| on sampled rows: {worst_exact:.4g}")
 
 
 def test_fp8_scale_zero_is_mean(fa):
