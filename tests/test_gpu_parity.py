@@ -253,14 +253,15 @@ def test_full_size_forward(fa, name):
     assert el <= TOL_LSE, f"LSE error {el:.4g}"
 
 
-def test_full_size_backward(fa):
-    """The forward+backward workload B=8, H=16, N=2048, d=128, causal: dQ, dK
-    and dV compared with the oracle on EVERY element of all 128 heads; whole
-    outputs written (prefilled with NaN), finite and bit-identical on a
-    repeated launch."""
+@pytest.mark.parametrize("name", ["bf16_b8h16n2048d128_causal_fwdbwd", "bf16_b16h32n1024d64_causal_fwdbwd"])
+def test_full_size_backward(fa, name):
+    """The forward+backward workloads the benchmark times (B=8 H=16 N=2048
+    d=128 causal, and B=16 H=32 N=1024 d=64 causal): dQ, dK and dV compared
+    with the oracle on EVERY element of every head; whole outputs written
+    (prefilled with NaN), finite and bit-identical on a repeated launch."""
     import torch
 
-    w = fi.WORKLOADS["bf16_b8h16n2048d128_causal_fwdbwd"]
+    w = fi.WORKLOADS.get(name) or fi.EXTRA_WORKLOADS[name]
     x = fi.make_inputs(w, with_grad=True)
     tq, tk, tv, tdo = (dev(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(tq, tk, tv, causal=True, scale=w.scale)
