@@ -28,6 +28,10 @@ pair of HIP events, and reported as the median and the minimum; a second
 series reads a 512 MiB scratch buffer before every launch, which evicts the
 L2 caches and the MALL, so that no input starts out on chip.
 
+The single-pass backward (fa_backward_atomic: dQ added with float32 atomics
+in the dK/dV pass) is timed beside fa_backward on the step's inputs
+(``series.fa_backward_atomic``); it is not part of the step.
+
 cpu_baseline: the fp64 oracle (materialising S and P) timed on the host on
 the first whole heads of the same workload, forward+backward, for about
 ``--cpu-seconds`` seconds.
@@ -348,11 +352,20 @@ def main():
 
     step_series = both_series(run_step, step_flops)
     backward_series = None
+    atomic_series = None
     if w.backward:
         backward_series = both_series(lambda: checked(fa.fa_backward(
             *(tensors[n].data_ptr() for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")),
             B, H, N, d, causal, scale, tensors["ws"].data_ptr(), tensors["ws"].numel(), sp), "backward"),
             w.bwd_flops())
+        # The single-pass form (dQ by float32 atomics in the dK/dV pass),
+        # timed on the same inputs; FLOPs counted as for fa_backward.
+        nat = fa.fa_backward_atomic_workspace_size(B, H, N, d)
+        ws_at = torch.empty(nat, dtype=torch.uint8, device=dev)
+        atomic_series = both_series(lambda: checked(fa.fa_backward_atomic(
+            *(tensors[n].data_ptr() for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")),
+            B, H, N, d, causal, scale, ws_at.data_ptr(), nat, sp), "backward_atomic"), w.bwd_flops())
+        del ws_at
 
     headline = []
     extra_backward = []
@@ -538,7 +551,7 @@ def main():
         "roofline": roofline,
         "kernels": kernel_table,
         "series": {"launches": SERIES_N, "flush_MiB": FLUSH_MIB, "step": step_series,
-                   "fa_backward": backward_series},
+                   "fa_backward": backward_series, "fa_backward_atomic": atomic_series},
         "gemm_reference": gemm_ref,
         "gemm_reference_fp8": gemm_ref_fp8,
         "headline_forward": headline,

@@ -16,7 +16,16 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import FA_ERR_TOO_LARGE, FA_ERR_UNSUPPORTED, FA_OK, NOALLOC_SCRATCH_BYTES, FaLibraryMissing, load  # noqa: F401
+from ._lib import (  # noqa: F401
+    FA_ERR_HIP,
+    FA_ERR_INVALID_ARG,
+    FA_ERR_TOO_LARGE,
+    FA_ERR_UNSUPPORTED,
+    FA_OK,
+    NOALLOC_SCRATCH_BYTES,
+    FaLibraryMissing,
+    load,
+)
 
 __all__ = [
     "FaError",
@@ -38,6 +47,9 @@ __all__ = [
     "fa_backward_dq_delta",
     "fa_backward_workspace_size",
     "fa_backward_noalloc",
+    "fa_backward_atomic",
+    "fa_backward_atomic_workspace_size",
+    "backward_atomic",
     "NOALLOC_SCRATCH_BYTES",
     "fa_status_string",
     "fa_abi_version",
@@ -141,6 +153,15 @@ def fa_backward_f32(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, 
 
 def fa_backward_workspace_size(B, H, N, d) -> int:
     return int(_call("fa_backward_workspace_size", B, H, N, d))
+
+
+def fa_backward_atomic_workspace_size(B, H, N, d) -> int:
+    return int(_call("fa_backward_atomic_workspace_size", B, H, N, d))
+
+
+def fa_backward_atomic(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes, stream) -> int:
+    return _call("fa_backward_atomic", q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, int(causal),
+                 float(scale), ws, ws_bytes, stream)
 
 
 def fa_backward_noalloc(q, k, v, o, lse, do, dq, dk, dv, B, H, N, d, causal, scale, stream) -> int:
@@ -340,6 +361,31 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv
+
+
+def backward_atomic(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, workspace=None):
+    """dQ, dK, dV from the single-pass backward (bf16 only): dK and dV equal
+    ``backward``'s bit for bit; dQ is accumulated with float32 atomics, so its
+    last bits depend on their order."""
+    import torch
+
+    if _check([q, k, v, o, do], ["q", "k", "v", "o", "do"]):
+        raise ValueError("backward_atomic takes bf16 tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    need = fa_backward_atomic_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_backward_atomic(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

@@ -428,6 +428,38 @@ int fa_forward_fp8(const void* q, const void* k, const void* v, const float* sig
                                        signs != nullptr, s), stream);
 }
 
+size_t fa_backward_atomic_workspace_size(int B, int H, int N, int d) {
+  const size_t rows_bytes = fa_backward_workspace_size(B, H, N, d);
+  if (rows_bytes == 0) return 0;
+  return rows_bytes + (size_t)B * (size_t)H * (size_t)N * (size_t)d * sizeof(float);
+}
+
+int fa_backward_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t elems = 0;
+  int st = check_common(B, H, N, d, causal, scale, true, &elems);
+  if (st != FA_OK) return st;
+  const size_t need = fa_backward_atomic_workspace_size(B, H, N, d);
+  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tb = elems * 2, lb = (size_t)B * H * N * sizeof(float);
+  const Span ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(lse, lb), span(dO, tb)};
+  const void* inp[6] = {q, k, v, o, lse, dO};
+  const Span outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(workspace, need)};
+  const void* outp[4] = {dq, dk, dv, workspace};
+  st = check_buffers(ins, inp, 6, outs, outp, 4);
+  if (st != FA_OK) return st;
+  float* delta = static_cast<float*>(workspace);
+  float* dqacc = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa_backward_workspace_size(B, H, N, d));
+  return hip_status(fa::launch_bwd_single_pass_bf16(
+                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse,
+                        static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+                        static_cast<uint16_t*>(dv), B * H, N, d, causal != 0, scale, delta, dqacc,
+                        static_cast<hipStream_t>(stream)),
+                    stream);
+}
+
 int fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, int d, int causal, float scale, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, causal, scale, stream, false);

@@ -26,6 +26,7 @@
 // zero key row contributes nothing to dQ, a query past N has a zero dO row
 // and delta (so dS = 0 and P^T dO = 0 whatever its P), and results for keys
 // or queries past N are never stored.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -189,17 +190,48 @@ __device__ __forceinline__ uint16_t* bwd_lds() {
   return buf;
 }
 
+// Single-pass form (dK/dV with dQ added by atomics): after the dK/dV
+// layout, the workgroup's K rows (read with the transpose read) and one
+// tile's dS, [128 keys][32 query slots].
+template <int D>
+struct SinglePassLds {
+  static constexpr int KS = row_read_stride<D>();
+  static constexpr int SS = 32 + 8;
+  static constexpr int K_OFF = DkdvLds<D>::ELEMS;
+  static constexpr int S_OFF = K_OFF + KV_BLK * KS;
+  static constexpr int ELEMS = S_OFF + KV_BLK * SS;
+  static_assert(ELEMS * 2 <= 160 * 1024, "the single-pass tiles fit in the LDS");
+};
+// Dynamic LDS (SinglePassLds<D>::ELEMS elements, set at launch): with a
+// static array the compiler would plan for the one workgroup per CU that
+// 119 KB allows at d = 128 and spread into the accumulator registers.
+__device__ __forceinline__ uint16_t* single_pass_lds() {
+  extern __shared__ __attribute__((aligned(16))) uint16_t sp_dyn_lds[];
+  return sp_dyn_lds;
+}
+
+// Barrier for LDS hazards only: this wave's LDS accesses are complete, its
+// vector memory operations may still be in flight (__syncthreads would also
+// wait for those).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // One workgroup's work for block id `wid` of a grid of `total` blocks.
-template <int D, bool CAUSAL>
+// ATOMIC: the single-pass form, which also adds this block's share of
+// dQ / scale (dS K over the block's 128 keys) into the float32 dQacc.
+template <int D, bool CAUSAL, bool ATOMIC = false>
 __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__ Q,
                                            const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                            const float* __restrict__ LSE, const uint16_t* __restrict__ dO,
                                            const float* __restrict__ delta, uint16_t* __restrict__ dK,
                                            uint16_t* __restrict__ dV, int N, int nkb, int total, float c,
-                                           float scale) {
+                                           float scale, float* __restrict__ dQacc = nullptr) {
   using L = DkdvLds<D>;
   constexpr int KSTEPS = D / 16, DB = D / 32;
-  uint16_t* smem = bwd_lds<D>();
+  uint16_t* smem;
+  if constexpr (ATOMIC)
+    smem = single_pass_lds();
+  else
+    smem = bwd_lds<D>();
   uint16_t* Vs = smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -213,6 +245,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t dqrs = make_rsrc(ATOMIC ? static_cast<const void*>(dQacc + base) : Q,
+                                                ATOMIC ? (uint32_t)N * D * 4 : 0u);
   const int k0 = kb * KV_BLK;
   const int kw = k0 + wave * 32;
   const int myk = kw + l32;
@@ -220,9 +254,10 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   // of the tile, i.e. qrow(r) + g
   auto qrow = [](int r) { return spread_row(8 * (r >> 2) + (r & 3)); };
 
-  // This lane's K row as the B operand of S = Q K^T (rows past N read as zero).
-  bf16x8 kf[KSTEPS];
-  {
+  // This lane's K row as the B operand of S = Q K^T (rows past N read as
+  // zero).  The single-pass form reads it from its K tile in LDS instead.
+  bf16x8 kf[ATOMIC ? 1 : KSTEPS];
+  if constexpr (!ATOMIC) {
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
@@ -232,6 +267,15 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   // here, stored to LDS after the first tile's loads are issued.
   Rows<KV_BLK, D> vrows;
   vrows.load(make_rsrc(V + base, head_bytes), k0, tid);
+  using SL = SinglePassLds<D>;
+  uint16_t* Ks = smem + SL::K_OFF;
+  uint16_t* Ss = smem + SL::S_OFF;
+  if constexpr (ATOMIC) {
+    // K rows for the dQ product (contracted over keys, so read transposed)
+    Rows<KV_BLK, D> krows;
+    krows.load(make_rsrc(K + base, head_bytes), k0, tid);
+    krows.template store<SL::KS>(Ks, tid);
+  }
 
   f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -301,7 +345,10 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     const float* dls = lse2 + 64;
     if (p + 1 < ntiles) fetch(qstart + tile_of(p + 1) * Q_TILE, smem + L::V_ELEMS + ((p + 1) & 1) * L::STAGE);
 
-    if (!CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
+    // (The single-pass form also runs tiles with no visible query for the
+    // wave, where P = 0 and the products add exact zeros: its dS rows must
+    // be written either way, and a skip branch there spills.)
+    if (ATOMIC || !CAUSAL || !MASK || qt0 + Q_TILE - 1 >= kw) {
       // S and dP: element r is query qt0 + qrow(r) + g, key myk.  At
       // d = 64 the dP accumulator starts from the tile's -delta values (the
       // workspace holds -delta), which saves a subtraction per element; at
@@ -319,14 +366,21 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        s = mfma32(row_operand<L::QS>(Qs, srow & 31, ks, g), kf[ks], ks == 0 ? f32x16{} : s);
+        bf16x8 kop;
+        if constexpr (ATOMIC)
+          kop = row_operand<SL::KS>(Ks, wave * 32 + l32, ks, g);
+        else
+          kop = kf[ks];
+        s = mfma32(row_operand<L::QS>(Qs, srow & 31, ks, g), kop, ks == 0 ? f32x16{} : s);
         dp = mfma32(row_operand<L::QS>(Gs, srow & 31, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
                     ks == 0 ? nd : dp);
       }
       // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
       // matrix-core instructions (mask 0x008), then 2 products per 3 reads
       // (deeper read-ahead does not fit the register budget at d = 128).
-      {
+      // The single-pass form leaves the order to the compiler: with a fourth
+      // read per step (its K rows) the fixed order spills at d = 128.
+      if constexpr (!ATOMIC) {
         constexpr int NM = 2 * KSTEPS, NR = 3 * KSTEPS, AH = 4, STEPS = (NR - AH) / 3;
         __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
@@ -373,17 +427,78 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         }
         __builtin_amdgcn_sched_group_barrier(0x008, AH / 2, 0);
       }
+      if constexpr (ATOMIC) {
+        // this wave's dS rows (the bf16 values of the dK product): row
+        // 32 wave + l%32, slot 8(r/4) + 4g + r%4 holds element r
+        __builtin_amdgcn_sched_barrier(0);
+        uint16_t* srow_p = Ss + (wave * 32 + l32) * SL::SS + 4 * g;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 w = __builtin_bit_cast(u32x4, acc_to_operand(dp, t));
+          *reinterpret_cast<u32x2*>(srow_p + 16 * t) = u32x2{w[0], w[1]};
+          *reinterpret_cast<u32x2*>(srow_p + 16 * t + 8) = u32x2{w[2], w[3]};
+        }
+      }
+    }
+    // dQ share of the tile: wave cb < D / 32 forms slots x columns
+    // 32 cb .. 32 cb + 31 over all 128 keys of the block (at d = 64 waves 2
+    // and 3 have no share: one atomic per element rather than two partial
+    // sums).  Both operands come from the transpose read with the same row
+    // order, so they pair key by key.
+    constexpr int NCB = D / 32;
+    const bool has_dq = wave < NCB;
+    if constexpr (ATOMIC) lds_barrier();
+    if (ATOMIC && has_dq) {
+      const int cb = wave;
+      f32x16 dq = {};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        dq = mfma32(tr_operand<SL::SS>(Ss, 16 * j, 0, 0, lane), tr_operand<SL::KS>(Ks, 16 * j, 32 * cb, 0, lane), dq);
+      // element r is slot m = 8(r/4) + 4g + r%4, i.e. query qt0 +
+      // spread_row(m) = qt0 + g + 16(a/2) + 2(a%2) + 4b (r = 4a + b),
+      // column 32 cb + l%32; rows past N fall outside the buffer and are
+      // dropped.  Exactly 16 atomics per wave per tile (the wait below
+      // counts on it).  The tile's base offset is opaque to the optimiser,
+      // so each atomic's offset stays base + constant (the constant's low
+      // 12 bits go to the instruction) instead of 16 offsets held across
+      // the loop.
+      uint32_t obase = (uint32_t)(((qt0 + g) * D + 32 * cb + l32) * 4);
+      asm volatile("" : "+v"(obase));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int a = r >> 2, b = r & 3;
+        const uint32_t rows = 16 * (a >> 1) + 2 * (a & 1) + 4 * b;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqrs, obase + rows * D * 4, 0, 0);
+      }
     }
     if (p + 1 < ntiles) put_lse(smem + L::V_ELEMS + ((p + 1) & 1) * L::STAGE);
-    wait_vmem();
-    __syncthreads();
+    if constexpr (ATOMIC) {
+      // Vector memory operations complete in issue order, so once at most
+      // the 16 atomics just issued are outstanding, the next tile's loads
+      // (issued before them) have landed; the atomics finish during the
+      // next tile.  A wave without atomics waits for everything.
+      if (has_dq)
+        __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
+      else
+        wait_vmem();
+      lds_barrier();
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
   };
   // Causal: the first KV_BLK / Q_TILE tiles straddle the diagonals of the
   // workgroup's waves; every later tile is fully visible.
   const int n_diag = CAUSAL ? min(ntiles, KV_BLK / Q_TILE) : 0;
-  int p = 0;
-  for (; p < ntiles - n_diag; ++p) step(p, std::false_type{});
-  for (; p < ntiles; ++p) step(p, std::true_type{});
+  if constexpr (ATOMIC) {
+    // one loop of masked steps (the mask is a no-op away from the
+    // diagonal): a second copy of the larger single-pass step spills
+    for (int p = 0; p < ntiles; ++p) step(p, std::true_type{});
+  } else {
+    int p = 0;
+    for (; p < ntiles - n_diag; ++p) step(p, std::false_type{});
+    for (; p < ntiles; ++p) step(p, std::true_type{});
+  }
 
   if (myk < N) {
     store_acc_row<D>(dK + base + (size_t)myk * D, dkt, scale, g);
@@ -634,6 +749,55 @@ bwd_fused_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dq_block<D, CAUSAL>(vid, Q, K, V, LSE, dO, delta, dQ, N, nb, total, c, scale);
 }
 
+// Single pass: dK/dV as bwd_dkdv_kernel (the same bits) and dQ / scale
+// added into dQacc (float32, zeroed beforehand) by atomics.  d = 128 holds
+// 119 KB of LDS, one workgroup per CU; d = 64 67 KB, two.
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_single_pass_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                       const uint16_t* __restrict__ V, const float* __restrict__ LSE,
+                       const uint16_t* __restrict__ dO, const float* __restrict__ delta,
+                       uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dQacc, int N,
+                       int nkb, int total, float c, float scale) {
+  dkdv_block<D, CAUSAL, true>(blockIdx.x, Q, K, V, LSE, dO, delta, dK, dV, N, nkb, total, c, scale, dQacc);
+}
+
+// n4 float4 of zeros.
+__global__ void __launch_bounds__(256) zero_f32_kernel(f32x4* __restrict__ p, long long n4) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) p[i] = f32x4{};
+}
+
+// dQ = bf16(scale * dQacc), 8 elements per thread (n8 groups).
+__global__ void __launch_bounds__(256) dq_convert_kernel(const f32x4* __restrict__ acc, u32x4* __restrict__ dq,
+                                                         long long n8, float scale) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    const f32x4 a = acc[2 * i], b = acc[2 * i + 1];
+    dq[i] = u32x4{pack_bf16x2(a[0] * scale, a[1] * scale), pack_bf16x2(a[2] * scale, a[3] * scale),
+                  pack_bf16x2(b[0] * scale, b[1] * scale), pack_bf16x2(b[2] * scale, b[3] * scale)};
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_single_pass(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
+                              const uint16_t* dO, const float* delta, uint16_t* dk, uint16_t* dv, float* dqacc,
+                              int BH, int N, float scale, hipStream_t stream) {
+  const int nkb = (N + KV_BLK - 1) / KV_BLK;
+  const long long tk = (long long)BH * nkb;
+  if (tk > 0x7fffffffLL || (long long)N * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  constexpr size_t lds_bytes = SinglePassLds<D>::ELEMS * 2;
+  // dynamic LDS above 64 KB: allowed once per kernel (thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&bwd_single_pass_kernel<D, CAUSAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((bwd_single_pass_kernel<D, CAUSAL>), dim3((unsigned)tk), dim3(NT), lds_bytes, stream, q, k, v,
+                     lse, dO, delta, dk, dv, dqacc, N, nkb, (int)tk, score_coef(scale), scale);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lse,
                        const uint16_t* dO, const float* delta, uint16_t* dk, uint16_t* dv, int BH,
@@ -722,6 +886,30 @@ hipError_t launch_bwd_dq_bf16(const uint16_t* q, const uint16_t* k, const uint16
     return causal ? launch_dq<128, true>(q, k, v, lse, dO, delta, dq, BH, N, scale, stream)
                   : launch_dq<128, false>(q, k, v, lse, dO, delta, dq, BH, N, scale, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_single_pass_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                      const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                                      uint16_t* dv, int BH, int N, int d, bool causal, float scale, float* delta,
+                                      float* dqacc, hipStream_t stream) {
+  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  const long long n = (long long)BH * N * d;   // a multiple of 64
+  const int cap = 256 * 8;
+  hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<long long>(cap, (n / 4 + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<f32x4*>(dqacc), n / 4);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (d == 64)
+    e = causal ? launch_single_pass<64, true>(q, k, v, lse, dO, delta, dk, dv, dqacc, BH, N, scale, stream)
+               : launch_single_pass<64, false>(q, k, v, lse, dO, delta, dk, dv, dqacc, BH, N, scale, stream);
+  else
+    e = causal ? launch_single_pass<128, true>(q, k, v, lse, dO, delta, dk, dv, dqacc, BH, N, scale, stream)
+               : launch_single_pass<128, false>(q, k, v, lse, dO, delta, dk, dv, dqacc, BH, N, scale, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)std::min<long long>(cap, (n / 8 + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<const f32x4*>(dqacc), reinterpret_cast<u32x4*>(dq), n / 8, scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -61,6 +61,15 @@ hipError_t launch_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t*
                            uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,
                            float scale, float* delta, hipStream_t stream);
 
+// Single-pass backward: -delta (row-dot pass) into `delta`, dqacc
+// (BH*N*d floats) zeroed, one dK/dV launch that also adds dS K into dqacc
+// with float32 atomics, then dq = bf16(scale * dqacc).  dK and dV have the
+// same bits as launch_bwd_bf16's; dQ depends on the order of the atomics.
+hipError_t launch_bwd_single_pass_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                                      const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                                      uint16_t* dv, int BH, int N, int d, bool causal, float scale, float* delta,
+                                      float* dqacc, hipStream_t stream);
+
 hipError_t launch_bwd_dkdv_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* lse, const uint16_t* dO, const float* delta,
                                 uint16_t* dk, uint16_t* dv, int BH, int N, int d, bool causal,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 enum fa_status {
   FA_OK = 0,
@@ -261,6 +261,34 @@ int fa_backward_dq_delta(const void* q, const void* k, const void* v, const void
 /* Bytes of workspace fa_backward and fa_backward_f32 need for these sizes
  * (0 if a size is not positive).  Pure host function. */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Single-pass backward (bf16 only): dK, dV and dQ from one pass over the
+ * (key block, query tile) pairs.  fa_backward's dQ pass recomputes S and dP
+ * for its own tiles; here the dK/dV pass, which has dS already, also adds
+ * each key block's share of dQ into a float32 accumulator with atomic adds.
+ * That takes 5 products of N x N x d per head instead of 7, at the price of
+ * the atomic traffic and of determinism (the recompute this replaces is the
+ * one of page "Flash Attention 2で打破するローカルLLMの「メモリの壁」：IO最適化の
+ * 実践的エンジニアリング", section 「タイリング（Tiling）と再計算（Recomputation）の
+ * 仕組み」; page "FlashAttention-2 — FlashAttention-2", section
+ * 「パフォーマンスと効率」, counts determinism among the method's properties,
+ * which is why fa_backward stays the default).
+ *   Arguments : as fa_backward; workspace of at least
+ *               fa_backward_atomic_workspace_size() bytes, 16-byte aligned
+ *               (the rows -delta_i, then a float32 [B][H][N][d] dQ
+ *               accumulator); its contents on entry are ignored.
+ *   Results   : dk and dv are bit-identical to fa_backward's.  dq =
+ *               bf16(scale * sum of the key blocks' shares): the float32
+ *               additions happen in the order the atomics arrive, so two
+ *               calls may differ in the last bits of dq.
+ *   Errors    : as fa_backward.
+ */
+size_t fa_backward_atomic_workspace_size(int B, int H, int N, int d);
+int fa_backward_atomic(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, int causal, float scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of the static device scratch buffer behind fa_backward_noalloc. */
 #define FA_NOALLOC_SCRATCH_BYTES (16u << 20)

@@ -46,3 +46,21 @@ def random_inputs(seed, shape, dtype, count, mult=1.0):
     if dtype == "bf16":
         return [fi.f32_to_bf16_bits(a) for a in arrs]
     return arrs
+
+
+def parallel(fn, tasks):
+    """Run fn over tasks on the host cores (numpy releases the GIL inside
+    its loops and products), with one BLAS thread per worker."""
+    import concurrent.futures as cf
+    import os
+
+    from threadpoolctl import threadpool_limits
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=1):
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, tasks))
+
+
+def report(name, what, err, floor, n):
+    print(f"PARITY {name} {what}: max_abs_err {err:.5g} storage_floor {floor:.5g} elements {n}", flush=True)

@@ -17,6 +17,8 @@ import pytest
 import fa_inputs as fi
 import oracle
 from tests.gpu_util import dev, host64, max_abs, random_inputs, storage_floor
+from tests.gpu_util import parallel as _parallel
+from tests.gpu_util import report as _report
 
 pytestmark = pytest.mark.gpu
 
@@ -192,24 +194,6 @@ def _sample_rows(N, n, rng):
     rows = {0, 1, N - 1, N - 2, N // 2}
     rows.update(rng.choice(N, size=min(n, N), replace=False).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < N))
-
-
-def _parallel(fn, tasks):
-    """Run fn over tasks on the host cores (numpy releases the GIL inside
-    its loops and products), with one BLAS thread per worker."""
-    import concurrent.futures as cf
-    import os
-
-    from threadpoolctl import threadpool_limits
-
-    workers = max(1, min(16, os.cpu_count() or 1))
-    with threadpool_limits(limits=1):
-        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-            return list(ex.map(fn, tasks))
-
-
-def _report(name, what, err, floor, n):
-    print(f"PARITY {name} {what}: max_abs_err {err:.5g} storage_floor {floor:.5g} elements {n}", flush=True)
 
 
 @pytest.mark.parametrize("name", FULL_FWD)
