@@ -6,7 +6,8 @@
 // With P = exp(scale*Q K^T - LSE) (masked entries 0) and delta = rowsum(dO * O):
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),
 //     dQ = scale * dS K,   dK = scale * dS^T Q.
-// Launches on one stream, no atomics, so the result is bit-reproducible:
+// The default backward launches on one stream with no atomics, so its
+// result is bit-reproducible:
 //   1. -delta (row-dot pre-pass, in f32_path.hip; the negated sums let the
 //      dP accumulators start from them), or computed by the dQ kernel for
 //      its own queries when that kernel runs first;
@@ -16,11 +17,14 @@
 //   3. dQ: one workgroup per (batch*head, 128 queries); each wave owns 32
 //      queries (Q and dO rows in registers) and loops over key tiles of 64
 //      (causal: up to the diagonal).
+// The single-pass form (bwd_single_pass_kernel) runs step 2 only and adds
+// each key block's share of dQ into a float32 accumulator with atomics; its
+// dK and dV are those of step 2, its dQ depends on the order of the adds.
 // Every product runs on the 32x32x16 bf16 matrix cores.  Each kernel picks
 // the orientation (S or S^T) in which its register-resident rows sit on the
 // lanes.  Tiles stay row-major in LDS; operands that need the other
 // orientation come from the LDS transpose read.  Tiles are double-buffered:
-// tile i+1 is fetched by direct HBM-to-LDS loads while tile i is computed
+// tile i+1 is fetched by direct HBM-to-LDS loads while tile i is computed.
 //
 // Ragged N needs no masks here: rows past N read as zero (buffer loads), a
 // zero key row contributes nothing to dQ, a query past N has a zero dO row
@@ -365,7 +369,7 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         }
       }
       // d = 128: the wave in a product phase gets issue priority over the
-      // other wave of its SIMD (2-3% faster dK/dV; at d = 64 ~1% slower)
+      // other wave of its SIMD (1.4-3.2% faster dK/dV; at d = 64 ~1% slower)
       if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
