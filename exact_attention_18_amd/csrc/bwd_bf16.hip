@@ -201,6 +201,7 @@ template <int D>
 struct SinglePassLds {
   static constexpr int KS = row_read_stride<D>();
   static constexpr int SS = 32 + 8;
+  static_assert(KS % 32 == 8 && SS % 32 == 8, "transpose reads 4 rows apart stay conflict free");
   static constexpr int K_OFF = DkdvLds<D>::ELEMS;
   static constexpr int S_OFF = K_OFF + KV_BLK * KS;
   static constexpr int ELEMS = S_OFF + KV_BLK * SS;
@@ -459,8 +460,9 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
     // dQ share of the tile: wave cb < D / 32 forms slots x columns
     // 32 cb .. 32 cb + 31 over all 128 keys of the block (at d = 64 waves 2
     // and 3 have no share: one atomic per element rather than two partial
-    // sums).  Both operands come from the transpose read with the same row
-    // order, so they pair key by key.
+    // sums).  Both operands come from the transpose read in the same
+    // (spread) row order, so they pair key by key; rows 4 apart at these
+    // strides (8 mod 32 elements) keep the reads free of bank conflicts.
     constexpr int NCB = D / 32;
     const bool has_dq = wave < NCB;
     if constexpr (ATOMIC) lds_barrier();
@@ -469,7 +471,8 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
       f32x16 dq = {};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        dq = mfma32(tr_operand<SL::SS>(Ss, 16 * j, 0, 0, lane), tr_operand<SL::KS>(Ks, 16 * j, 32 * cb, 0, lane), dq);
+        dq = mfma32(tr_operand_spread<SL::SS>(Ss, 32 * (j >> 1), 0, j & 1, lane),
+                    tr_operand_spread<SL::KS>(Ks, 32 * (j >> 1), 32 * cb, j & 1, lane), dq);
       // element r is slot m = 8(r/4) + 4g + r%4, i.e. query qt0 +
       // spread_row(m) = qt0 + g + 16(a/2) + 2(a%2) + 4b (r = 4a + b),
       // column 32 cb + l%32; rows past N fall outside the buffer and are
