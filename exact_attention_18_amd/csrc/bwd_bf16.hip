@@ -606,39 +606,28 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
   // accumulators start from it
   float ndl;
   if constexpr (DELTA) {
-    // 16 lanes per row, 16 rows per pass; the values go to HBM for the dK/dV
-    // kernel and, through LDS past the tiles, to the lanes that own the rows.
-    static_assert(DqLds<D>::ELEMS + 2 * Q_BLK <= bwd_lds_elems<D>(), "no room for the row sums");
-    float* nds = reinterpret_cast<float*>(smem + DqLds<D>::ELEMS);
+    // The lane holds columns 16 ks + 8 g .. + 7 of its dO row (gf); it
+    // loads the same columns of its O row, sums their products as one FMA
+    // chain in column order, and adds the other half from lane ^ 32.  The
+    // row-dot pass (rowdot_bf16_kernel) sums in the same order, so both give
+    // the same bits.
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(O + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
-    const int part = tid & 15;
+    u32x4 orow[KSTEPS];
 #pragma unroll
-    for (int it = 0; it < Q_BLK / (NT / 16); ++it) {
-      const int rl = it * (NT / 16) + (tid >> 4), row = q0 + rl;
-      float acc = 0.f;
-      if (row < N) {
-        for (int col = part * 8; col < D; col += 128) {
-          const u32x4 a = buf_load16(ors, (uint32_t)((row * D + col) * 2));
-          const u32x4 b = buf_load16(grs, (uint32_t)((row * D + col) * 2));
+    for (int ks = 0; ks < KSTEPS; ++ks) orow[ks] = buf_load16(ors, (uint32_t)((myq * D + ks * 16 + 8 * g) * 2));
+    float part = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(b[w]), acc);
-            acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(b[w]), acc);
-          }
-        }
-      }
-      acc += __shfl_xor(acc, 8);
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 1);
-      if (part == 0) {
-        if (row < N) nd_out[(size_t)bh * N + row] = -acc;
-        nds[rl] = row < N ? -acc : 0.f;
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 gw = __builtin_bit_cast(u32x4, gf[ks]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        part = __builtin_fmaf(bf16_lo(orow[ks][w]), bf16_lo(gw[w]), part);
+        part = __builtin_fmaf(bf16_hi(orow[ks][w]), bf16_hi(gw[w]), part);
       }
     }
-    __syncthreads();
-    ndl = nds[wave * 32 + l32];
+    const float tot = part + __shfl_xor(part, 32);
+    ndl = myq < N ? -tot : 0.f;
+    if (g == 0 && myq < N) nd_out[(size_t)bh * N + myq] = ndl;
   } else {
     ndl = myq < N ? delta[(size_t)bh * N + myq] : 0.f;
   }

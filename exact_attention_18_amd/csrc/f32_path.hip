@@ -246,11 +246,12 @@ bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, cons
 }
 
 // delta: 16 threads per row, each summing 16-byte chunks part, part+16, ...
-// NEG stores -delta (the bf16 kernels start their dP accumulators from it).
+// NEG stores -delta.  (float32 rows; bf16 rows use rowdot_bf16_kernel.)
 template <typename T, bool NEG>
 __global__ void __launch_bounds__(NT)
 rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restrict__ delta,
               long long rows, int d) {
+  static_assert(sizeof(T) == 4, "float32 rows");
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   const long long row = (long long)blockIdx.x * (NT / 16) + (threadIdx.x >> 4);
   const int part = threadIdx.x & 15;
@@ -261,18 +262,9 @@ rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restric
     for (int col = part * EPC; col < d; col += 16 * EPC) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(o + col);
       const u32x4 b = *reinterpret_cast<const u32x4*>(g + col);
-      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x = word_of(a, w), y = word_of(b, w);
-          acc = __builtin_fmaf(bf16_lo(x), bf16_lo(y), acc);
-          acc = __builtin_fmaf(bf16_hi(x), bf16_hi(y), acc);
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          acc = __builtin_fmaf(__uint_as_float(word_of(a, w)), __uint_as_float(word_of(b, w)), acc);
-      }
+      for (int w = 0; w < 4; ++w)
+        acc = __builtin_fmaf(__uint_as_float(word_of(a, w)), __uint_as_float(word_of(b, w)), acc);
     }
   }
   acc += __shfl_xor(acc, 8);
@@ -280,6 +272,48 @@ rowdot_kernel(const T* __restrict__ O, const T* __restrict__ G, float* __restric
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 1);
   if (row < rows && part == 0) delta[row] = NEG ? -acc : acc;
+}
+
+// bf16 delta (negated when NEG) in the order the dQ kernel uses for its own
+// queries: per row, two halves (columns 16 k + 8 h .. + 7, h = 0, 1), each
+// summed as one FMA chain in column order, then added.  One wave per 32
+// rows: the rows are copied to LDS with consecutive lanes on consecutive
+// 16-byte chunks, then lane 2 r + h sums half h of row r.
+constexpr int RD_ROWS = 32;
+template <bool NEG>
+__global__ void __launch_bounds__(64)
+rowdot_bf16_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ G, float* __restrict__ delta,
+                   long long rows, int d) {
+  __shared__ __attribute__((aligned(16))) uint16_t so[RD_ROWS * 128], sg[RD_ROWS * 128];
+  const long long r0 = (long long)blockIdx.x * RD_ROWS;
+  const int lane = threadIdx.x;
+  const int cpr = d / 8;   // 16-byte chunks per row
+  for (int ch = lane; ch < RD_ROWS * cpr; ch += 64) {
+    const long long row = r0 + ch / cpr;
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (row < rows) {
+      a = *reinterpret_cast<const u32x4*>(O + row * d + (ch % cpr) * 8);
+      b = *reinterpret_cast<const u32x4*>(G + row * d + (ch % cpr) * 8);
+    }
+    *reinterpret_cast<u32x4*>(so + ch * 8) = a;
+    *reinterpret_cast<u32x4*>(sg + ch * 8) = b;
+  }
+  __syncthreads();
+  const int rl = lane >> 1, h = lane & 1;
+  float acc = 0.f;
+  for (int k = 0; k < d / 16; ++k) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(so + rl * d + 16 * k + 8 * h);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(sg + rl * d + 16 * k + 8 * h);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = word_of(a, w), y = word_of(b, w);
+      acc = __builtin_fmaf(bf16_lo(x), bf16_lo(y), acc);
+      acc = __builtin_fmaf(bf16_hi(x), bf16_hi(y), acc);
+    }
+  }
+  const float tot = acc + __shfl_xor(acc, 1);
+  const long long row = r0 + rl;
+  if (row < rows && h == 0) delta[row] = NEG ? -tot : tot;
 }
 
 template <typename T, bool NEG>
@@ -294,7 +328,11 @@ hipError_t launch_rowdot(const T* o, const T* g, float* delta, long long rows, i
 
 hipError_t launch_rowdot_bf16(const uint16_t* o, const uint16_t* dO, float* delta, long long rows,
                               int d, hipStream_t stream) {
-  return launch_rowdot<uint16_t, true>(o, dO, delta, rows, d, stream);
+  if (d % 16 != 0 || d > 128) return hipErrorInvalidValue;
+  const long long blocks = (rows + RD_ROWS - 1) / RD_ROWS;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rowdot_bf16_kernel<true>), dim3((unsigned)blocks), dim3(64), 0, stream, o, dO, delta, rows, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowdot_f32(const float* o, const float* dO, float* delta, long long rows, int d,
