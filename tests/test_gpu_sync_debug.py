@@ -28,7 +28,8 @@ def fa():
 
 def _run_all(fa):
     """Forward, backward, decode, block-sparse and FP8 on small ragged shapes;
-    returns every output as a host array."""
+    returns every output as a host array, and the single-pass backward's
+    outputs separately (its dQ depends on the order of its atomic adds)."""
     import torch
 
     out = []
@@ -42,19 +43,24 @@ def _run_all(fa):
     mask = torch.from_numpy(fi.random_block_mask(6, nqb, 0.5)).to(q.device)
     ob, lb = fa.forward_block_sparse(q, k, v, mask)
     o8, l8 = fa.forward_fp8(q, k, v, dev(fi.random_signs(0, d)))
+    aq, ak, av = fa.backward_atomic(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
-    for t in (o, lse, dq, dk, dv, od, ld, ob, lb, o8, l8):
+    for t in (o, lse, dq, dk, dv, od, ld, ob, lb, o8, l8, ak, av):
         out.append(t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy())
-    return out
+    return out, aq.float().cpu().numpy()
 
 
 def test_sync_debug_same_results(fa):
     os.environ.pop("FA_SYNC_DEBUG", None)
-    ref = _run_all(fa)
+    ref, ref_aq = _run_all(fa)
     os.environ["FA_SYNC_DEBUG"] = "1"
     try:
-        got = _run_all(fa)
+        got, got_aq = _run_all(fa)
     finally:
         os.environ.pop("FA_SYNC_DEBUG", None)
     for a, b in zip(ref, got):
         assert np.array_equal(a, b, equal_nan=True)
+    # the single-pass dK and dV are compared above with the rest; its dQ
+    # (order-dependent float32 sums, then bf16) within one bf16 step
+    assert np.all(np.isfinite(got_aq))
+    assert float(np.max(np.abs(ref_aq - got_aq))) <= 1e-2
