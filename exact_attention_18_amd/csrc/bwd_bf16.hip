@@ -901,6 +901,9 @@ hipError_t launch_bwd_single_pass_bf16(const uint16_t* q, const uint16_t* k, con
                                       uint16_t* dv, int BH, int N, int d, bool causal, float scale, float* delta,
                                       float* dqacc, hipStream_t stream) {
   if (d != 64 && d != 128) return hipErrorInvalidValue;
+  // the single-pass launch's limits, checked before anything is launched
+  const long long tk = (long long)BH * ((N + KV_BLK - 1) / KV_BLK);
+  if (tk > 0x7fffffffLL || (long long)N * d * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   const long long n = (long long)BH * N * d;   // a multiple of 64
   const int cap = 256 * 8;
   hipError_t e = launch_rowdot_bf16(o, dO, delta, (long long)BH * N, d, stream);
