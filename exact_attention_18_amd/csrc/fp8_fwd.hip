@@ -477,12 +477,18 @@ hipError_t launch_fp8_prepare(const uint16_t* q, const uint16_t* k, const uint16
   const Fp8Buffer L = fp8_buffer_layout(BH, N);
   uint8_t* base = static_cast<uint8_t*>(buf);
   const long long rows = (long long)BH * L.Np;
+  const long long vt = (long long)BH * (L.Np / 32) * (FD / 4);
+  // the limits of these launches and of launch_fwd_fp8, checked before
+  // anything is launched (fa_forward_fp8 runs this first)
+  const long long nqb = (N + FBR - 1) / FBR;
+  if ((rows + 63) / 64 > 0x7fffffffLL || (vt + 255) / 256 > 0x7fffffffLL || (long long)BH * nqb > 0x7fffffffLL ||
+      (long long)L.Np * FD >= (1LL << 31))
+    return hipErrorInvalidValue;
   const unsigned rb = (unsigned)((rows + 63) / 64);   // 64 rows per workgroup
   hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rb), dim3(256), 0, stream, q, signs, base + L.q8, base + L.qe, N,
                      L.Np, rows);
   hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(rb), dim3(256), 0, stream, k, signs, base + L.k8, base + L.ke, N,
                      L.Np, rows);
-  const long long vt = (long long)BH * (L.Np / 32) * (FD / 4);
   hipLaunchKernelGGL(fp8_quant_v_kernel, dim3((unsigned)((vt + 255) / 256)), dim3(256), 0, stream, v, base + L.v8,
                      base + L.ve, N, L.Np, vt);
   return hipGetLastError();
