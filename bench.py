@@ -206,7 +206,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the attention kernels on a single "
+        print("bench.py measures one GPU only: the library runs the attention kernels on a single "
               "MI355X and has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
