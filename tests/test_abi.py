@@ -136,6 +136,55 @@ def test_backward_rejects_overlaps_and_small_workspace(lib):
     assert bwd(lib, ws_bytes=need - 1) == INVALID
 
 
+def atomic(lib, B=1, H=1, N=8, d=64, causal=0, scale=0.125, ptrs=None, ws_bytes=None):
+    p = ptrs or [ptr(i) for i in range(10)]
+    if ws_bytes is None:
+        ws_bytes = lib.fa_backward_atomic_workspace_size(B, H, N, d)
+    return lib.fa_backward_atomic(*p[:9], B, H, N, d, causal, scale, p[9], ws_bytes, None)
+
+
+def test_backward_atomic_workspace_size(lib):
+    # the rows -delta (rounded to 256 bytes), then the float32 dQ accumulator
+    assert lib.fa_backward_atomic_workspace_size(8, 16, 2048, 128) == 8 * 16 * 2048 * 4 + 8 * 16 * 2048 * 128 * 4
+    assert lib.fa_backward_atomic_workspace_size(1, 1, 1, 64) == 256 + 64 * 4
+    assert lib.fa_backward_atomic_workspace_size(0, 1, 1, 64) == 0
+    assert lib.fa_backward_atomic_workspace_size(1, 1, -5, 64) == 0
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_backward_atomic_rejects_null_and_misaligned(lib, which):
+    p = [ptr(i) for i in range(10)]
+    p[which] = None
+    assert atomic(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(10)]
+    p[which] = ptr(which, 4)
+    assert atomic(lib, ptrs=p) == INVALID
+
+
+def test_backward_atomic_rejects_bad_arguments(lib):
+    assert atomic(lib, d=96) == UNSUP
+    assert atomic(lib, N=0) == INVALID
+    assert atomic(lib, causal=2) == INVALID
+    need = lib.fa_backward_atomic_workspace_size(1, 1, 8, 64)
+    assert atomic(lib, ws_bytes=need - 1) == INVALID
+    p = [ptr(i) for i in range(10)]
+    p[9] = p[6]  # workspace on dq
+    assert atomic(lib, ptrs=p) == INVALID
+    p = [ptr(i) for i in range(10)]
+    p[8] = p[0] + 64  # dv inside q
+    assert atomic(lib, ptrs=p) == INVALID
+
+
+def test_backward_atomic_too_large_is_refused_before_launch(lib):
+    # One head of 2^23 rows of d = 128: 2 GiB per tensor, past the 32-bit
+    # buffer offsets of the kernels.  Each tensor fits its own 4 GiB window
+    # and the 4 GiB workspace sits apart, so the host checks pass and the
+    # launcher refuses the size before any HIP call.
+    N, d = 1 << 23, 128
+    p = [ptr(2 * i) for i in range(9)] + [ptr(40)]
+    assert atomic(lib, N=N, d=d, ptrs=p) == _lib.FA_ERR_HIP
+
+
 def test_python_binding_names_match_abi():
     import exact_attention_18_amd as fa
 
