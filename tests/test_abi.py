@@ -326,6 +326,17 @@ def test_fp8_rejects_overlaps(lib):
     assert lib.fa_forward_fp8_prepared(ptr(6), need, ptr(6) + 32, ptr(5), 1, 1, 100, 128, 0, 0.1, 1, None) == INVALID
 
 
+def test_fp8_too_large_is_refused_before_launch(lib):
+    # One head of 2^24 rows of d = 128: 4 GiB per bf16 tensor, past the
+    # 32-bit offsets of the FP8 attention kernel.  Each buffer gets its own
+    # window (q, k, v, o: 4 GiB each; the prepared buffer, ~6.4 GiB, far
+    # apart), so the host checks pass and the one-call entry refuses the size
+    # before it launches the quantisation.
+    N = 1 << 24
+    p = [ptr(2 * i) for i in range(6)] + [ptr(60)]
+    assert fp8_fwd(lib, N=N, ptrs=p) == _lib.FA_ERR_HIP
+
+
 def test_block_sparse_workspace(lib):
     need = lib.fa_block_sparse_workspace_size(1, 1, 300, 64)
     assert need > 0 and lib.fa_block_sparse_workspace_size(1, 1, 300, 96) == 0
