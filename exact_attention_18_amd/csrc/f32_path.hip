@@ -359,11 +359,14 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
                           const float* lse, const float* dO, float* dq, float* dk, float* dv,
                           int BH, int N, int d, bool causal, float scale, float* delta,
                           hipStream_t stream) {
-  hipError_t e = launch_rowdot_f32(o, dO, delta, (long long)BH * N, d, stream);
-  if (e != hipSuccess) return e;
   const int nb = (N + ROWS - 1) / ROWS;
   const long long blocks = (long long)BH * nb;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  // checked before the row-dot pass is launched, so a refused problem
+  // launches nothing
+  if (blocks > 0x7fffffffLL || ((long long)BH * N + (NT / 16) - 1) / (NT / 16) > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  hipError_t e = launch_rowdot_f32(o, dO, delta, (long long)BH * N, d, stream);
+  if (e != hipSuccess) return e;
   const float c = scale * kLog2e;
   if (causal) {
     hipLaunchKernelGGL(bwd_dkdv_f32_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, q, k, v,
