@@ -240,16 +240,14 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   uint16_t* Vs = smem;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NT / 64 - 1);  // wave-uniform, below 4
   const int l32 = lane & 31, g = lane >> 5;
   int bh, kb;
   map_block(wid, total, nkb, CAUSAL ? 2 : 0, bh, kb);  // causal: low key blocks carry the most work
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(LSE + (size_t)bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  const RowSrc<D> qrs{Q + base, head_bytes}, grs{dO + base, head_bytes};
+  const RowSrc<1, float> lrs{LSE + (size_t)bh * N, (uint32_t)N * 4}, drs{delta + (size_t)bh * N, (uint32_t)N * 4};
   const __amdgpu_buffer_rsrc_t dqrs = make_rsrc(ATOMIC ? static_cast<const void*>(dQacc + base) : Q,
                                                 ATOMIC ? (uint32_t)N * D * 4 : 0u);
   const int k0 = kb * KV_BLK;
@@ -308,16 +306,18 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
   uint32_t lse_bits = 0;
   const int srow = (lane & 32) | spread_row(l32);
   auto fetch = [&](int qt0, uint16_t* stage) {
+    const __amdgpu_buffer_rsrc_t qr = qrs.from_row(qt0), gr = grs.from_row(qt0);
 #pragma unroll
     for (int u = 0; u < NJ; ++u) {
       const int j = wave + 4 * u;
       if (j < 2 * L::RI) {
         const int m = j / L::RI, jj = j % L::RI;
-        lds_load16(m ? grs : qrs, stage + m * L::TILE + jj * 512, voff[u] + (uint32_t)qt0 * D * 2);
+        lds_load16(m ? gr : qr, stage + m * L::TILE + jj * 512, voff[u]);
       }
     }
-    if (wave == 2) lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs, (uint32_t)(qt0 + srow) * 4, 0, 0);
-    if (wave == 3) lds_load4(drs, stage + 2 * L::TILE + 128, (uint32_t)(qt0 + srow) * 4);
+    if (wave == 2)
+      lse_bits = __builtin_amdgcn_raw_buffer_load_b32(lrs.from_row(qt0), (uint32_t)srow * 4, 0, 0);
+    if (wave == 3) lds_load4(drs.from_row(qt0), stage + 2 * L::TILE + 128, (uint32_t)srow * 4);
   };
   auto put_lse = [&](uint16_t* stage) {
     if (wave == 2) reinterpret_cast<float*>(stage + 2 * L::TILE)[lane] = __uint_as_float(lse_bits) * kLog2e;
@@ -552,14 +552,13 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
   uint16_t* smem = bwd_lds<D>();
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NT / 64 - 1);  // wave-uniform, below 4
   const int l32 = lane & 31, g = lane >> 5;
   int bh, qb;
   map_block_xcd(wid, total, nqb, CAUSAL, bh, qb);
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+  const RowSrc<D> krs{K + base, head_bytes}, vrs{V + base, head_bytes};
   const int q0 = qb * Q_BLK;
   const int qw = q0 + wave * 32;
   const int myq = qw + l32;
@@ -592,13 +591,14 @@ __device__ __forceinline__ void dq_block(int wid, const uint16_t* __restrict__ Q
     voff[u] = col < D / 8 ? (uint32_t)(row * D + col * 8) * 2 : 0x80000000u;
   }
   auto fetch = [&](int kv0, uint16_t* stage) {
+    const __amdgpu_buffer_rsrc_t kr = krs.from_row(kv0), vr = vrs.from_row(kv0);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int j = wave + 4 * u;
       if (j < L::KLOADS)
-        lds_load16(krs, stage + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
+        lds_load16(kr, stage + j * 512, voff[u]);
       else if (j < NL)
-        lds_load16(vrs, stage + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
+        lds_load16(vr, stage + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u]);
     }
   };
   fetch(0, smem);   // the first tiles load while -delta is computed

@@ -63,6 +63,20 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
 }
 
+// The rows of one (batch, head) matrix, [N][W] elements of type T, as a
+// buffer source.  from_row(r) is a buffer resource that starts at row r, so
+// the per-lane offsets of a tile load stay the same from tile to tile (the
+// tile's start moves into the scalar base address, not into every lane's
+// offset); reads at or past row N still return zero.  Needs r <= N.
+template <int W, typename T = uint16_t>
+struct RowSrc {
+  const T* p;
+  uint32_t bytes;   // N * W * sizeof(T)
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t from_row(int r) const {
+    return make_rsrc(p + (size_t)r * W, bytes - (uint32_t)r * W * (uint32_t)sizeof(T));
+  }
+};
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane s supplies the address of 4 consecutive bf16 (a row segment); lane i
 // of the group receives element i%4 of the segments of lanes i/4, i/4+4,

@@ -383,7 +383,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QE, c
   using L = Fp8Lds;
   __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (FNT / 64 - 1);  // wave-uniform, below 4
   const int l32 = lane & 31, h = lane >> 5;
   int bh, qb;
   map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);

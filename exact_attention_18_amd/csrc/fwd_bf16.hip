@@ -85,15 +85,16 @@ struct TileDma {
     }
   }
   // Tile starting at key kv0 into the stage at dst (K, then V at K_ELEMS).
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kv0,
-                                        uint16_t* dst, int wave) const {
+  __device__ __forceinline__ void issue(const RowSrc<D>& ks, const RowSrc<D>& vs, int kv0, uint16_t* dst,
+                                        int wave) const {
+    const __amdgpu_buffer_rsrc_t kr = ks.from_row(kv0), vr = vs.from_row(kv0);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int j = wave + NW * u;
       if (j < L::KLOADS)
-        lds_load16(kr, dst + j * 512, voff[u] + (uint32_t)kv0 * D * 2);
+        lds_load16(kr, dst + j * 512, voff[u]);
       else if (j < NL)
-        lds_load16(vr, dst + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u] + (uint32_t)kv0 * D * 2);
+        lds_load16(vr, dst + L::K_ELEMS + (j - L::KLOADS) * 512, voff[u]);
     }
   }
 };
@@ -101,8 +102,10 @@ struct TileDma {
 // Online-softmax bookkeeping for one wave's 64-key tile of S^T (element r of
 // s[kb] is key 32*kb + 8*(r/4) + 4*g + r%4): optional mask (keys past `lim`
 // get -inf), row max, and the lazy rescale of the reference max m, the row
-// sum and the output accumulators.
-template <int D, bool MASK, int NKB = 2>
+// sum and the output accumulators.  FIRST: the wave's first tile, where m is
+// still -inf and the row sum and accumulators are still zero, so the rescale
+// by alpha = 2^-inf = 0 would leave them unchanged and is skipped.
+template <int D, bool MASK, int NKB = 2, bool FIRST = false>
 __device__ __forceinline__ void softmax_update(f32x16 (&s)[NKB], f32x16 (&oacc)[D / 32], float& m, float& lsum,
                                                float c, int lim) {
   if (MASK) {
@@ -134,11 +137,13 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[NKB], f32x16 (&oacc)[
   // more than TAU; otherwise p stays below 2^TAU and nothing is rescaled.
   if (__any(mx > m + TAU)) {
     const float mn = fmaxf(m, mx);
-    const float alpha = exp2_hw(m - mn);
-    m = mn;
-    lsum *= alpha;
+    if constexpr (!FIRST) {
+      const float alpha = exp2_hw(m - mn);
+      lsum *= alpha;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    }
+    m = mn;
   }
 }
 
@@ -150,7 +155,9 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[NKB], f32x16 (&oacc)[
 // keeps m.  Otherwise (also while m is still -inf, which gives inf or NaN)
 // the tile takes softmax_update and P is recomputed with the new m, as if
 // the fast path had not run.  Sums are added in the same order either way.
-template <int D, bool MASK, int NKB = 2>
+// FIRST (the wave's first tile, m still -inf, where the fast path always
+// fails): straight to softmax_update, with the same arithmetic and bits.
+template <int D, bool MASK, int NKB = 2, bool FIRST = false>
 __device__ __forceinline__ void softmax_probs(f32x16 (&s)[NKB], u32x4 (&pw)[2 * NKB], f32x16 (&oacc)[D / 32],
                                               float& m, float& lsum, float c, int lim) {
   if (MASK) {
@@ -182,11 +189,17 @@ __device__ __forceinline__ void softmax_probs(f32x16 (&s)[NKB], u32x4 (&pw)[2 * 
     return bmax;
   };
   float l = lsum;
-  const float bmax = probs(l);
-  if (__any(!(bmax <= PMAX))) {
-    softmax_update<D, false, NKB>(s, oacc, m, lsum, c, 0);
+  if constexpr (FIRST) {
+    softmax_update<D, false, NKB, true>(s, oacc, m, lsum, c, 0);
     l = lsum;
     probs(l);
+  } else {
+    const float bmax = probs(l);
+    if (__any(!(bmax <= PMAX))) {
+      softmax_update<D, false, NKB>(s, oacc, m, lsum, c, 0);
+      l = lsum;
+      probs(l);
+    }
   }
   lsum = l;
 }
@@ -194,8 +207,8 @@ __device__ __forceinline__ void softmax_probs(f32x16 (&s)[NKB], u32x4 (&pw)[2 * 
 // One 64-key tile for one wave: S^T = K Q^T, (mask), online softmax update,
 // O^T += V^T P^T.  MASK selects the variant for tiles that straddle the
 // diagonal or the end of N; `lim` is the largest visible key offset within
-// the tile for this lane's query, minus 4*g.
-template <int D, bool MASK>
+// the tile for this lane's query, minus 4*g.  FIRST: the wave's first tile.
+template <int D, bool MASK, bool FIRST = false>
 __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs, const bf16x8 (&qf)[D / 16],
                                           f32x16 (&oacc)[D / 32], float& m, float& lsum, float c, int lim,
                                           int lane) {
@@ -229,7 +242,7 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 
   u32x4 pw[4];
-  softmax_probs<D, MASK>(s, pw, oacc, m, lsum, c, lim);
+  softmax_probs<D, MASK, 2, FIRST>(s, pw, oacc, m, lsum, c, lim);
 
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -253,15 +266,15 @@ __device__ __forceinline__ void tile_step(const uint16_t* Ks, const uint16_t* Vs
 // the LDS accesses alias scopes, so the compiler can tell that the transpose
 // reads of this tile do not read what the loads write and does not make
 // them wait for the loads.
-template <int D, bool MASK, int NW>
+template <int D, bool MASK, int NW, bool FIRST = false>
 __device__ __forceinline__ void tile_step_next(const uint16_t* __restrict__ Ks, const uint16_t* __restrict__ Vs,
                                                uint16_t* __restrict__ next, bool load_next,
-                                               const TileDma<D, NW>& dma, __amdgpu_buffer_rsrc_t krs,
-                                               __amdgpu_buffer_rsrc_t vrs, int kv_next, int wave,
+                                               const TileDma<D, NW>& dma, const RowSrc<D>& krs,
+                                               const RowSrc<D>& vrs, int kv_next, int wave,
                                                const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& m,
                                                float& lsum, float c, int lim, int lane) {
   if (load_next) dma.issue(krs, vrs, kv_next, next, wave);
-  tile_step<D, MASK>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
+  tile_step<D, MASK, FIRST>(Ks, Vs, qf, oacc, m, lsum, c, lim, lane);
 }
 
 #ifndef FA_FWD_WAVES_PER_SIMD
@@ -288,14 +301,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  // wave-uniform, kept in an SGPR; the mask tells the compiler it is below 4,
+  // which settles at compile time which tile loads each wave issues
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NT / 64 - 1);
   const int l32 = lane & 31, g = lane >> 5;
   int bh, qb;
   map_block_xcd(blockIdx.x, total, nqb, CAUSAL, bh, qb);
   const size_t base = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+  const RowSrc<D> krs{K + base, head_bytes}, vrs{V + base, head_bytes};
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
   const int q0 = qb * BR;
   const int qw = q0 + wave * 32;   // first query of this wave
@@ -371,10 +385,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // Interior tiles (no key of the tile is hidden from any query of the
   // workgroup) run the unmasked step; the remaining tiles (at most two on the
   // causal diagonal, or the ragged last tile) run the masked one.  Two loops
-  // rather than a branch per tile keep the accumulators in place.
+  // rather than a branch per tile keep the accumulators in place.  Tile 0
+  // holds key 0, which every query sees, and is the first of every wave: it
+  // takes the FIRST step (row max at once, m being still -inf).
   const int n_plain = min(CAUSAL ? q0 / BC : ntiles, N / BC);
-  auto step = [&](int j, auto mask_tag) {
+  auto step = [&](int j, auto mask_tag, auto first_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const uint16_t* Ks = smem + (j & 1) * L::STAGE;
     const uint16_t* Vs = Ks + L::K_ELEMS;
     uint16_t* next = smem + ((j + 1) & 1) * L::STAGE;
@@ -382,21 +399,25 @@ fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if constexpr (MASK) {
       if (!CAUSAL || kv0 <= qw + 31) {
         const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * g;
-        tile_step_next<D, true, NT / 64>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf, oacc, m,
-                                        lsum, c, lim, lane);
+        tile_step_next<D, true, NT / 64, FIRST>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf,
+                                               oacc, m, lsum, c, lim, lane);
       } else if (j + 1 < ntiles) {
         dma.issue(krs, vrs, kv0 + BC, next, wave);
       }
     } else {
-      tile_step_next<D, false, NT / 64>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf, oacc, m,
-                                       lsum, c, 0, lane);
+      tile_step_next<D, false, NT / 64, FIRST>(Ks, Vs, next, j + 1 < ntiles, dma, krs, vrs, kv0 + BC, wave, qf,
+                                              oacc, m, lsum, c, 0, lane);
     }
     wait_vmem();
     __syncthreads();
   };
-  int j = 0;
-  for (; j < n_plain; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  int j = 1;
+  if (n_plain > 0)
+    step(0, std::false_type{}, std::true_type{});
+  else
+    step(0, std::true_type{}, std::true_type{});
+  for (; j < n_plain; ++j) step(j, std::false_type{}, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{}, std::false_type{});
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
@@ -912,7 +933,7 @@ fwd_sparse_balanced_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t smem[L::ELEMS];
   __shared__ long long s_item;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NT / 64 - 1);
   const int l32 = lane & 31, g = lane >> 5;
   const int P = plan[0];
   const int* row_cnt = plan + 4;
@@ -943,8 +964,7 @@ fwd_sparse_balanced_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     // this item's visible blocks: ordinals [o0, o1) among the row's visible blocks
     const int o0 = (int)((long long)part * cnt / parts), o1 = (int)((long long)(part + 1) * cnt / parts);
     const size_t base = (size_t)bh * N * D;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+    const RowSrc<D> krs{K + base, head_bytes}, vrs{V + base, head_bytes};
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
     const int q0 = qb * BR, qw = q0 + wave * 32, myq = qw + l32;
     bf16x8 qf[KSTEPS];
