@@ -147,6 +147,15 @@ __device__ __forceinline__ void store_acc_row(uint16_t* __restrict__ dst_row, co
 }
 
 // ---------------------------------------------------------------- dK / dV
+// LDS reads the dK/dV step issues ahead of its products: row-operand reads
+// ahead of the S / dP products, transpose reads ahead of the dV / dK
+// products.  Measured (balanced A/B, B8 H16 N2048 d128 causal dK/dV): 7 and 8
+// at d = 128 took 284 us against 292 for 4 and 4; at d = 64, 8 transpose
+// reads ahead were 2% slower than 4.
+template <int D>
+constexpr int dkdv_row_reads_ahead() { return 7; }
+template <int D>
+constexpr int dkdv_tr_reads_ahead() { return D == 128 ? 8 : 4; }
 constexpr int KV_BLK = 128;   // keys per dK/dV workgroup
 constexpr int Q_TILE = 32;    // queries per dK/dV tile
 constexpr int Q_BLK = 128;    // queries per dQ workgroup
@@ -383,13 +392,13 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
         dp = mfma32(row_operand<L::QS>(Gs, srow & 31, ks, g), row_operand<L::VS>(Vs, wave * 32 + l32, ks, g),
                     ks == 0 ? nd : dp);
       }
-      // Scheduling: 4 row-operand LDS reads (mask 0x100) ahead of the
-      // matrix-core instructions (mask 0x008), then 2 products per 3 reads
-      // (deeper read-ahead does not fit the register budget at d = 128).
-      // The single-pass form leaves the order to the compiler: with a fourth
-      // read per step (its K rows) the fixed order spills at d = 128.
+      // Scheduling: dkdv_row_reads_ahead row-operand LDS reads (mask 0x100)
+      // ahead of the matrix-core instructions (mask 0x008), then 2 products
+      // per 3 reads.  The single-pass form leaves the order to the compiler:
+      // with a fourth read per step (its K rows) the fixed order spills at
+      // d = 128.
       if constexpr (!ATOMIC) {
-        constexpr int NM = 2 * KSTEPS, NR = 3 * KSTEPS, AH = 4, STEPS = (NR - AH) / 3;
+        constexpr int NM = 2 * KSTEPS, NR = 3 * KSTEPS, AH = dkdv_row_reads_ahead<D>(), STEPS = (NR - AH) / 3;
         __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
         for (int u = 0; u < STEPS; ++u) {
@@ -429,9 +438,9 @@ __device__ __forceinline__ void dkdv_block(int wid, const uint16_t* __restrict__
           dkt[db] = mfma32(tr_operand_spread<L::QS>(Qs, 0, 32 * db, t, lane), dsb, dkt[db]);
         }
       }
-      // 4 transpose reads ahead, then one product per 2 reads.
+      // dkdv_tr_reads_ahead transpose reads ahead, then one product per 2 reads.
       {
-        constexpr int NM = 4 * DB, AH = 4;
+        constexpr int NM = 4 * DB, AH = dkdv_tr_reads_ahead<D>();
         __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
         for (int u = 0; u < NM - AH / 2; ++u) {
