@@ -257,29 +257,34 @@ struct Fp8TileDma {
       voff[u] = o;
     }
   }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t k8, __amdgpu_buffer_rsrc_t ke,
-                                        __amdgpu_buffer_rsrc_t v8, __amdgpu_buffer_rsrc_t ve, int kv0, uint8_t* st,
-                                        int wave) const {
+  // Tile starting at key kv0 (a multiple of FBC, below Np): the buffer
+  // resources start at the tile (K and V codes kv0 * FD bytes in, their
+  // scales kv0 * 4), so the per-lane offsets stay the same from tile to tile.
+  __device__ __forceinline__ void issue(const RowSrc<FD, uint8_t>& k8s, const RowSrc<1, uint32_t>& kes,
+                                        const RowSrc<FD, uint8_t>& v8s, const RowSrc<1, uint32_t>& ves, int kv0,
+                                        uint8_t* st, int wave) const {
+    const __amdgpu_buffer_rsrc_t k8 = k8s.from_row(kv0), ke = kes.from_row(kv0);
+    const __amdgpu_buffer_rsrc_t v8 = v8s.from_row(kv0), ve = ves.from_row(kv0);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int j = wave + 4 * u;
       if (j < KL)
-        lds_load16(k8, reinterpret_cast<uint16_t*>(st + 1024 * j), voff[u] + (uint32_t)kv0 * FD);
+        lds_load16(k8, reinterpret_cast<uint16_t*>(st + 1024 * j), voff[u]);
       else if (j == KL)
-        lds_load4(ke, reinterpret_cast<uint16_t*>(st + L::K_BYTES), voff[u] + (uint32_t)kv0 * 4);
+        lds_load4(ke, reinterpret_cast<uint16_t*>(st + L::K_BYTES), voff[u]);
       else if (j < NL - 1)
-        lds_load16(v8, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + 1024 * (j - KL - 1)),
-                   voff[u] + (uint32_t)(kv0 / FBC) * FD * 64);
+        lds_load16(v8, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + 1024 * (j - KL - 1)), voff[u]);
       else if (j == NL - 1)
-        lds_load4(ve, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + L::V_BYTES),
-                  voff[u] + (uint32_t)(kv0 / FBC) * 256);
+        lds_load4(ve, reinterpret_cast<uint16_t*>(st + L::K_BYTES + L::KE_BYTES + L::V_BYTES), voff[u]);
     }
   }
 };
 
 // One 64-key tile for this wave's 32 queries (same online softmax as the
-// bf16 forward; see fwd_bf16.hip).
-template <bool MASK>
+// bf16 forward; see fwd_bf16.hip).  FIRST: the wave's first tile, where m is
+// still -inf (the fast path would always fail) and the row sum and the
+// accumulators are still zero (the rescale would leave them unchanged).
+template <bool MASK, bool FIRST = false>
 __device__ __forceinline__ void fp8_tile_step(const uint8_t* st, const v8i* qf, uint32_t qsc, f32x16* oacc, float& m,
                                               float& lsum, float c, int lim, int lane) {
   using L = Fp8Lds;
@@ -331,7 +336,7 @@ __device__ __forceinline__ void fp8_tile_step(const uint8_t* st, const v8i* qf, 
                    max_nan(max_nan(ps[4], ps[5]), max_nan(ps[6], ps[7])));
   };
   float l = lsum;
-  if (__any(!(probs(l) <= 256.f))) {
+  if (FIRST || __any(!(probs(l) <= 256.f))) {
     float m8[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -346,11 +351,13 @@ __device__ __forceinline__ void fp8_tile_step(const uint8_t* st, const v8i* qf, 
     mx = max_halves(mx) * c;
     if (__any(mx > m + FTAU)) {
       const float mn = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mn);
-      m = mn;
-      lsum *= alpha;
+      if constexpr (!FIRST) {
+        const float alpha = exp2_hw(m - mn);
+        lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < FD / 32; ++i) oacc[i] *= alpha;
+        for (int i = 0; i < FD / 32; ++i) oacc[i] *= alpha;
+      }
+      m = mn;
     }
     l = lsum;
     probs(l);
@@ -391,10 +398,11 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QE, c
   const uint32_t code_bytes = (uint32_t)Np * FD;
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q8 + rows0 * FD, code_bytes);
   const __amdgpu_buffer_rsrc_t qes = make_rsrc(QE + rows0 * 4, (uint32_t)Np * 4);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K8 + rows0 * FD, code_bytes);
-  const __amdgpu_buffer_rsrc_t kes = make_rsrc(KE + rows0 * 4, (uint32_t)Np * 4);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V8 + rows0 * FD, code_bytes);
-  const __amdgpu_buffer_rsrc_t ves = make_rsrc(VE + rows0 * 4, (uint32_t)Np * 4);
+  // V's codes are stored in blocks of 64 keys x FD bytes, so a tile of V
+  // starts kv0 * FD bytes in, as K's does.
+  const RowSrc<FD, uint8_t> krs{K8 + rows0 * FD, code_bytes}, vrs{V8 + rows0 * FD, code_bytes};
+  const RowSrc<1, uint32_t> kes{reinterpret_cast<const uint32_t*>(KE + rows0 * 4), (uint32_t)Np * 4},
+      ves{reinterpret_cast<const uint32_t*>(VE + rows0 * 4), (uint32_t)Np * 4};
   const int q0 = qb * FBR;
   const int qw = q0 + wave * 32;
   const int myq = qw + l32;
@@ -422,21 +430,27 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QE, c
   wait_vmem();
   __syncthreads();
   const int n_plain = min(CAUSAL ? q0 / FBC : ntiles, N / FBC);
-  auto step = [&](int j, auto mask_tag) {
+  // Tile 0 holds key 0, which every query sees, and is every wave's first.
+  auto step = [&](int j, auto mask_tag, auto first_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const uint8_t* st = smem + (j & 1) * L::STAGE;
     const int kv0 = j * FBC;
     if (j + 1 < ntiles) dma.issue(krs, kes, vrs, ves, kv0 + FBC, smem + ((j + 1) & 1) * L::STAGE, wave);
     if (!MASK || !CAUSAL || kv0 <= qw + 31) {
       const int lim = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * h;
-      fp8_tile_step<MASK>(st, qf, qsc, oacc, m, lsum, c, lim, lane);
+      fp8_tile_step<MASK, FIRST>(st, qf, qsc, oacc, m, lsum, c, lim, lane);
     }
     wait_vmem();
     __syncthreads();
   };
-  int j = 0;
-  for (; j < n_plain; ++j) step(j, std::false_type{});
-  for (; j < ntiles; ++j) step(j, std::true_type{});
+  int j = 1;
+  if (n_plain > 0)
+    step(0, std::false_type{}, std::true_type{});
+  else
+    step(0, std::true_type{}, std::true_type{});
+  for (; j < n_plain; ++j) step(j, std::false_type{}, std::false_type{});
+  for (; j < ntiles; ++j) step(j, std::true_type{}, std::false_type{});
 
   const float ltot = sum_halves(lsum);
   const float inv = rcp_hw(ltot);
