@@ -200,7 +200,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 plain copies of MIB MiB (for counter calibration)")
     ap.add_argument("--print-digest", action="store_true", help="print the kernel source digest and exit")
+    ap.add_argument("--progress", action="store_true", help="print a line to stderr as each part finishes")
     args = ap.parse_args()
+
+    def note(msg):
+        if args.progress:
+            print(f"bench: {msg}", file=sys.stderr, flush=True)
     if args.print_digest:
         print(kernel_source_digest())
         return
@@ -350,7 +355,9 @@ def main():
             out[key] = sr
         return out
 
+    note(f"timed steps done ({ms_per_step:.4f} ms per step)")
     step_series = both_series(run_step, step_flops)
+    note("step series done")
     backward_series = None
     atomic_series = None
     if w.backward:
@@ -376,6 +383,7 @@ def main():
             ht, hk = step_kernels(hw, False)
             sr = both_series(lambda: checked(hk[0][1](), "fwd"), hw.fwd_flops())
             tf = sr["warm"]["tflops_median"]
+            note(f"forward {name} done")
             headline.append({"workload": name, "kernel": "fwd", "ms": sr["warm"]["median_ms"], "tflops": tf,
                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "series": sr})
             del ht, hk
@@ -392,6 +400,7 @@ def main():
                 ew.B, ew.H, ew.N, ew.d, int(ew.causal), ew.scale, et["ws"].data_ptr(), et["ws"].numel(), sp),
                 "backward"), ew.bwd_flops())
             estep = both_series(lambda: run_kernels(ek), ew.fwd_flops() + ew.bwd_flops())
+            note(f"backward {name} done")
             extra_backward.append({"workload": name, "fa_backward": ebw, "step": estep})
             del et, ek
 
@@ -416,6 +425,7 @@ def main():
             dms = series(lambda: checked(fa.fa_forward(
                 *args_, bw.B, bw.H, bw.N, bw.d, int(bw.causal), bw.scale, sp), "fwd"), False)["median_ms"]
             tf = sw.fwd_flops() / (sms * 1e-3) / 1e12
+            note(f"block-sparse {name} done")
             block_sparse.append({"workload": name, "kernel": "fwd_block_sparse",
                                  "density": round(float(sw.mask().mean()), 4), "ms": round(sms, 4),
                                  "tflops_visible": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -444,6 +454,7 @@ def main():
                 hb.data_ptr(), nb, ho.data_ptr(), hl.data_ptr(), hw.B, hw.H, hw.N, hw.d, int(hw.causal), hw.scale,
                 1, sp), "fp8_forward"), False)["median_ms"]
             tf = hw.fwd_flops() / (fms * 1e-3) / 1e12
+            note(f"FP8 forward {name} done")
             fp8.append({"workload": name, "kernel": "fwd_fp8", "prepare_ms": round(pms, 4), "ms": round(fms, 4),
                         "tflops": round(tf, 1), "peak_fp8": PEAK_FP8_TFLOPS,
                         "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
@@ -466,6 +477,7 @@ def main():
                 dw.Nq, dw.Nk, dw.d, int(dw.causal), dw.scale, dws.data_ptr(), dws_bytes, sp), "decode"), True)
             dms = dsr["median_ms"]
             gbs = dw.hbm_bytes() / (dms * 1e-3) / 1e9
+            note(f"decode {name} done")
             decode.append({"workload": name, "entry": "fa_decode", "ms": round(dms, 4), "flushed": True,
                            "algorithmic_bytes": dw.hbm_bytes(), "GB_per_s": round(gbs, 1),
                            "hbm_peak_GB_per_s": PEAK_HBM_GBS, "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
@@ -479,6 +491,7 @@ def main():
     gb_ = torch.randn(GEMM_REF_N, GEMM_REF_N, device=dev, dtype=torch.bfloat16)
     gemm_ms = series(lambda: torch.matmul(ga_, gb_), False)["median_ms"]
     gemm_tf = 2.0 * GEMM_REF_N ** 3 / (gemm_ms * 1e-3) / 1e12
+    note("vendor bf16 GEMM done")
     gemm_ref = {"op": f"torch.matmul bf16 {GEMM_REF_N}x{GEMM_REF_N}x{GEMM_REF_N} (hipBLASLt)",
                 "median_ms": round(gemm_ms, 4), "tflops": round(gemm_tf, 1),
                 "frac_of_peak": round(gemm_tf / PEAK_BF16_TFLOPS, 4)}
